@@ -1,0 +1,250 @@
+/*
+ * pkv — grouped-query attention read through a paged KV cache, for AMD
+ * Instinct MI355X (gfx950).  C ABI: plain pointers, sizes and status codes.
+ *
+ * Model of the cache ("Tiered KV cache — architecture", section "The
+ * paged-attention block model"): tokens are stored in fixed-size physical
+ * blocks; a per-sequence logical->physical block table says which block
+ * holds which range of positions; an entry equal to PKV_INVALID_BLOCK_ID is
+ * a hole whose positions score -infinity, i.e. do not exist (also section
+ * "Kernel dispatch").  A block is block_size tokens x n_kv_heads x head_dim
+ * of K and of V (section "The three-tier model").
+ *
+ * Windows ("KV Cache Design — cells, format, sessions", section 1
+ * "Positions and cells"): causal positions, one [lo, hi) range per
+ * sequence, or a map of up to PKV_KV_MAP_MAX_SPANS (cell, len) runs, read
+ * in place, so a copy-on-write prefix shared by several sequences is read
+ * through identical block ids without copies.
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device memory owned by the caller.  The library
+ *    never allocates device memory and keeps no pointer after a call
+ *    returns; scratch comes in through a caller-owned workspace whose size
+ *    the matching *_workspace_bytes call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *    stream) unless stated; inputs must stay alive until the stream passes.
+ *  - Every argument the host can check is checked before anything is
+ *    launched, so a refused call writes nothing ("KV Cache Design", section
+ *    4: verify before apply).  Refusals return a status code and set a
+ *    message readable with pkv_last_error() (per thread).  The library never
+ *    aborts the process.
+ *  - Device-resident integers (block ids, lengths, windows, positions) are
+ *    not read back.  They are clamped where they are used: a window outside
+ *    [0, seq_len) is clipped, seq_len is clipped to max_blocks_per_seq *
+ *    block_size, and a block id outside [-1, n_pool_blocks) is treated as a
+ *    hole, so no input makes a kernel read or write outside its buffers.
+ *    With PKV_FLAG_CHECKED such ids are also reported: the call then waits
+ *    for the stream and returns PKV_E_ARG.
+ *  - No internal locking ("Tiered KV cache — architecture", section "The
+ *    single-threading contract"): one caller mutates a pool at a time;
+ *    calls on one stream are ordered.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sentinel for a wiped logical block (a hole). */
+#define PKV_INVALID_BLOCK_ID (-1)
+/* Most (cell, len) runs one kv_map window may hold. */
+#define PKV_KV_MAP_MAX_SPANS 8
+/* pkv_shape.flags: validate device ids and report bad ones (slow: syncs). */
+#define PKV_FLAG_CHECKED 1u
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_E_ARG = 1,         /* malformed argument (null, negative, mismatch) */
+  PKV_E_UNSUPPORTED = 2, /* well formed but outside the dispatch table   */
+  PKV_E_WORKSPACE = 3,   /* workspace missing or too small                */
+  PKV_E_DEVICE = 4       /* a HIP call failed                             */
+} pkv_status;
+
+/* KV storage formats ("KV Cache Design", section 3: f32, f16, q8_0). */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_Q8_0 = 2 } pkv_fmt;
+
+/* Window modes; the mode fixes the shape of the window input. */
+typedef enum {
+  PKV_WIN_CAUSAL = 0, /* window = NULL: positions [0, seq_len)                */
+  PKV_WIN_SPAN = 1,   /* window = int32 [n_seqs][2] = (lo, hi)                */
+  PKV_WIN_KV_MAP = 2  /* window = int32 [n_seqs][n_runs][2] = (cell, len);
+                         len <= 0 marks an unused run; runs may overlap and a
+                         position listed twice counts twice                   */
+} pkv_win;
+
+/*
+ * Geometry of one attention call.
+ *
+ * Pools: k_pool and v_pool are [n_pool_blocks][block_size][row] where a row
+ * is one token's entries for all kv heads: [n_kv_heads][head_dim] values for
+ * f32/f16, or pkv_row_bytes(PKV_Q8_0, ...) bytes for q8_0 (per kv head,
+ * head_dim/32 blocks of a little-endian f16 scale followed by 32 int8
+ * codes; value = scale * code).  Pool row r = block * block_size + slot.
+ * block_table: int32 [n_seqs][max_blocks_per_seq].  seq_lens: int32
+ * [n_seqs].  q head h reads kv head h / (n_q_heads / n_kv_heads).
+ * Scores are scale * q.k.
+ *
+ * Supported ("Tiered KV cache — architecture", sections "The
+ * paged-attention block model" and "Kernel dispatch"): (head_dim,
+ * block_size) in {(64,16), (128,16), (256,16), (128,32)}; n_q_heads /
+ * n_kv_heads in {1, 2, 3, 4, 8}; (q, K, V) formats in {(f32, f32, f32),
+ * (f16, f16, f16), (f16, q8_0, f16), (f32, q8_0, f32)}.  Anything else is
+ * refused with PKV_E_UNSUPPORTED and a message naming the tuple.
+ */
+typedef struct {
+  int32_t n_seqs;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t n_pool_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t q_fmt; /* pkv_fmt: PKV_F32 or PKV_F16 */
+  int32_t k_fmt; /* pkv_fmt */
+  int32_t v_fmt; /* pkv_fmt: PKV_F32 or PKV_F16 */
+  float scale;
+  uint32_t flags;       /* PKV_FLAG_* */
+  int32_t split_tokens; /* decode split size in tokens; 0 = automatic; else a
+                           multiple of block_size, at most 64 blocks */
+} pkv_shape;
+
+/* Bytes of one pool row (one token, all kv heads) in format fmt; 0 when the
+ * arguments are invalid.  A q8_0 row is rounded up to whole 4-byte words
+ * ("KV Cache Design", section 3). */
+int64_t pkv_row_bytes(int32_t fmt, int32_t n_kv_heads, int32_t head_dim);
+
+/* ---------------------------------------------------------------------------
+ * Decode: one query per sequence, at position seq_len - 1, seeing
+ * W_s intersected with [0, seq_len) minus holes ("KV cache" (sipllm),
+ * section "Problem": a decode step dots the new query against the stored
+ * history).  Split-K: each (sequence, kv head, split of the window) is a
+ * separate work item producing (max, sum, unnormalised output); a second
+ * pass merges the splits by log-sum-exp.  The split size depends only on
+ * the shape, so results are deterministic and do not change when blocks
+ * move in the pool and the table follows.
+ *
+ * q:   [n_seqs][n_q_heads][head_dim] in q_fmt.
+ * out: float32 [n_seqs][n_q_heads][head_dim] = sum_t w_t v_t / sum_t w_t.
+ * lse: float32 [n_seqs][n_q_heads] natural-log log-sum-exp of the scores,
+ *      or NULL.  An empty visible set gives out = 0 and lse = -inf.
+ * workspace: device, at least pkv_decode_workspace_bytes(...) bytes, 256-byte
+ *      aligned; its contents need no initialisation.
+ * ------------------------------------------------------------------------- */
+size_t pkv_decode_workspace_bytes(const pkv_shape* shape, int32_t mode, int32_t n_runs);
+
+/* Split size in tokens that a decode call with this shape uses (0 if the
+ * shape is refused). */
+int32_t pkv_decode_split_tokens(const pkv_shape* shape, int32_t mode, int32_t n_runs);
+
+pkv_status pkv_paged_attn_decode(const pkv_shape* shape, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t mode, int32_t n_runs,
+                                 const int32_t* window, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* The two passes of pkv_paged_attn_decode as separate calls (same arguments;
+ * the partials live in the workspace between them).  Lets a caller time or
+ * overlap the passes; partials followed by merge equals the fused call. */
+pkv_status pkv_paged_attn_decode_partials(const pkv_shape* shape, const void* q,
+                                          const void* k_pool, const void* v_pool,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          int32_t mode, int32_t n_runs, const int32_t* window,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_attn_decode_merge(const pkv_shape* shape, const int32_t* seq_lens,
+                                       int32_t mode, int32_t n_runs, const int32_t* window,
+                                       float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Windowed prefill: a chunk of queries per sequence against its window,
+ * causal inside the window ("KV Cache Design", section 1: the fast windowed
+ * prefill families for more than one query).  QK^T and PV run on the matrix
+ * cores.  Query j of sequence s sees W_s intersected with
+ * [0, min(seq_len_s, q_pos_j + 1)) minus holes.
+ *
+ * n_q_total: rows of q.  cu_q: int32 [n_seqs + 1], queries of sequence s are
+ * rows cu_q[s] .. cu_q[s+1]-1 (non-decreasing, cu_q[0] = 0, cu_q[n_seqs] =
+ * n_q_total; rows outside are left untouched).  max_q_per_seq: an upper
+ * bound on cu_q[s+1] - cu_q[s] (queries past it are not computed).
+ * q_pos: int32 [n_q_total] position of each query in its sequence.
+ * q: [n_q_total][n_q_heads][head_dim] in q_fmt; out float32 same shape; lse
+ * float32 [n_q_total][n_q_heads] or NULL.
+ * ------------------------------------------------------------------------- */
+size_t pkv_prefill_workspace_bytes(const pkv_shape* shape, int32_t n_q_total,
+                                   int32_t max_q_per_seq, int32_t mode, int32_t n_runs);
+
+pkv_status pkv_paged_attn_prefill_window(const pkv_shape* shape, int32_t n_q_total,
+                                         int32_t max_q_per_seq, const void* q,
+                                         const int32_t* cu_q, const int32_t* q_pos,
+                                         const void* k_pool, const void* v_pool,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         int32_t mode, int32_t n_runs, const int32_t* window,
+                                         float* out, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Row moves ("KV Cache Design", section 2: a compaction changes only cells,
+ * so rows move verbatim; whoever copies must apply the moves in order_moves
+ * order — upward moves top-down, downward moves bottom-up, upward first —
+ * because a destination may never land on a row not yet copied).
+ *
+ * A move is int32 (src, dst, len) in pool rows; dst > src is "up".  Upward
+ * moves are ordered by descending src (then descending dst), downward moves
+ * by ascending src (then ascending dst), ties by input index; moves with
+ * dst == src or len <= 0 are no-ops and left out.  For move sets with no
+ * safe order the result is defined as applying the ordered moves one after
+ * another, each as a memmove.
+ * ------------------------------------------------------------------------- */
+
+/* Host only.  moves: host int32 [n][3].  order_out: host int32 [n]; receives
+ * the indices of the effective moves in application order; *n_out their
+ * count. */
+pkv_status pkv_order_moves(const int32_t* moves, int32_t n, int32_t* order_out, int32_t* n_out);
+
+/* Workspace for pkv_kv_copy_cells with these moves (an upper bound). */
+size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t row_bytes_k,
+                                      int64_t row_bytes_v);
+
+/* Apply moves (host int32 [n][3]) to k_pool and, if not NULL, v_pool
+ * (device, n_pool_rows rows of row_bytes_k / row_bytes_v bytes; row bytes
+ * a multiple of 4), bit-exact.  The host plans the moves (order_moves, then
+ * the final source of every changed row), uploads the plan into the
+ * workspace and waits for that upload, so `moves` may be freed on return;
+ * the copies themselves run asynchronously on `stream`.  Every move must
+ * lie inside [0, n_pool_rows) or the call is refused untouched. */
+pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int64_t n_pool_rows,
+                             int64_t row_bytes_k, int64_t row_bytes_v, const int32_t* moves,
+                             int32_t n, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Debug export of the block-table/window resolver the attention kernels use.
+ * rows_out: int32 [n_q_total][n_cand]: for query j and candidate index i of
+ * its sequence's window enumeration (causal: positions 0..seq_len-1; span:
+ * lo..hi-1; kv_map: the concatenation of its runs with len > 0) the pool
+ * row that slot reads, or -1 when the index is past the enumeration, the
+ * position is outside [0, min(seq_len, q_pos + 1)) or it lies in a hole.
+ * Decode (cu_q == NULL and q_pos == NULL): n_q_total == n_seqs, query s at
+ * position seq_len_s - 1.  Prefill: cu_q / q_pos as for prefill.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_resolve_rows(const pkv_shape* shape, int32_t n_q_total, const int32_t* cu_q,
+                            const int32_t* q_pos, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t mode, int32_t n_runs,
+                            const int32_t* window, int32_t n_cand, int32_t* rows_out,
+                            void* stream);
+
+/* Message of the last refused call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,339 @@
+"""Paged GQA attention for MI355X (gfx950): Python binding of libpkv.so.
+
+Every function here only marshals torch tensors into the C ABI declared in
+include/pkv.h (pointers, sizes, the current HIP stream) and calls it; all
+computation runs in the library's HIP kernels.  If the library is missing,
+or a call is refused, the call raises: there is no fallback path.
+
+Formats follow the tensors' dtypes: float32 -> f32, float16 -> f16, and a
+uint8 K pool of shape [n_blocks, block_size, row_bytes] -> q8_0.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpkv.so")
+
+F32, F16, Q8_0 = 0, 1, 2
+WIN_CAUSAL, WIN_SPAN, WIN_KV_MAP = 0, 1, 2
+MODES = {"causal": WIN_CAUSAL, "span": WIN_SPAN, "kv_map": WIN_KV_MAP}
+FLAG_CHECKED = 1
+INVALID_BLOCK_ID = -1
+KV_MAP_MAX_SPANS = 8
+
+STATUS = {0: "PKV_OK", 1: "PKV_E_ARG", 2: "PKV_E_UNSUPPORTED", 3: "PKV_E_WORKSPACE", 4: "PKV_E_DEVICE"}
+
+# Every symbol include/pkv.h declares.
+EXPORTS = (
+    "pkv_row_bytes",
+    "pkv_decode_workspace_bytes",
+    "pkv_decode_split_tokens",
+    "pkv_paged_attn_decode",
+    "pkv_paged_attn_decode_partials",
+    "pkv_paged_attn_decode_merge",
+    "pkv_prefill_workspace_bytes",
+    "pkv_paged_attn_prefill_window",
+    "pkv_order_moves",
+    "pkv_copy_cells_workspace_bytes",
+    "pkv_kv_copy_cells",
+    "pkv_resolve_rows",
+    "pkv_last_error",
+    "pkv_version",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_pool_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("q_fmt", ctypes.c_int32),
+        ("k_fmt", ctypes.c_int32),
+        ("v_fmt", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("split_tokens", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_table_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SH = ctypes.POINTER(Shape)
+    sig = {
+        "pkv_row_bytes": (I64, [I32, I32, I32]),
+        "pkv_decode_workspace_bytes": (SZ, [SH, I32, I32]),
+        "pkv_decode_split_tokens": (I32, [SH, I32, I32]),
+        "pkv_paged_attn_decode": (I32, [SH, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
+        "pkv_paged_attn_decode_partials": (I32, [SH, P, P, P, P, P, I32, I32, P, P, SZ, P]),
+        "pkv_paged_attn_decode_merge": (I32, [SH, P, I32, I32, P, P, P, P, SZ, P]),
+        "pkv_prefill_workspace_bytes": (SZ, [SH, I32, I32, I32, I32]),
+        "pkv_paged_attn_prefill_window": (I32, [SH, I32, I32, P, P, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
+        "pkv_order_moves": (I32, [P, I32, P, P]),
+        "pkv_copy_cells_workspace_bytes": (SZ, [P, I32, I64, I64]),
+        "pkv_kv_copy_cells": (I32, [P, P, I64, I64, I64, P, I32, P, SZ, P]),
+        "pkv_resolve_rows": (I32, [SH, I32, P, P, P, P, I32, I32, P, I32, P, P]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+        "pkv_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise PkvError(status, lib().pkv_last_error().decode())
+
+
+def last_error() -> str:
+    return lib().pkv_last_error().decode()
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _fmt_of(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.uint8:
+        return Q8_0
+    raise TypeError(f"no KV format for dtype {t.dtype}")
+
+
+def _i32(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def row_bytes(fmt: int, n_kv_heads: int, head_dim: int) -> int:
+    return int(lib().pkv_row_bytes(fmt, n_kv_heads, head_dim))
+
+
+def make_shape(q, k_pool, v_pool, block_table, n_seqs: int, scale: float, flags: int = 0,
+               split_tokens: int = 0) -> Shape:
+    """pkv_shape from the tensors: q [.., Hq, hd]; v_pool [NB, bs, Hkv, hd]."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if not t.is_contiguous():
+            raise TypeError(f"{name} must be contiguous")
+    _i32(block_table, "block_table")
+    if v_pool.dim() != 4:
+        raise TypeError("v_pool must be [n_blocks, block_size, n_kv_heads, head_dim]")
+    nb, bs, hkv, hd = v_pool.shape
+    return Shape(n_seqs=n_seqs, n_q_heads=q.shape[-2], n_kv_heads=hkv, head_dim=hd, block_size=bs,
+                 n_pool_blocks=nb, max_blocks_per_seq=block_table.shape[1], q_fmt=_fmt_of(q),
+                 k_fmt=_fmt_of(k_pool), v_fmt=_fmt_of(v_pool), scale=scale, flags=flags,
+                 split_tokens=split_tokens)
+
+
+def _window_args(mode: str, window):
+    m = MODES[mode]
+    if m == WIN_CAUSAL:
+        return m, 1, None
+    if window is None:
+        raise ValueError(f"mode {mode} needs a window tensor")
+    _i32(window, "window")
+    n_runs = window.shape[1] if m == WIN_KV_MAP else 1
+    return m, n_runs, window
+
+
+def _workspace(nbytes: int, like, workspace):
+    torch = _torch()
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=like.device)
+
+
+# ---------------------------------------------------------------------------
+# attention
+
+
+def decode_workspace_bytes(shape: Shape, mode: str = "causal", n_runs: int = 1) -> int:
+    return int(lib().pkv_decode_workspace_bytes(ctypes.byref(shape), MODES[mode], n_runs))
+
+
+def decode_split_tokens(shape: Shape, mode: str = "causal", n_runs: int = 1) -> int:
+    return int(lib().pkv_decode_split_tokens(ctypes.byref(shape), MODES[mode], n_runs))
+
+
+def paged_attn_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, mode: str = "causal",
+                      window=None, out=None, lse=None, workspace=None, flags: int = 0,
+                      split_tokens: int = 0, part: str = "both"):
+    """Decode attention (one query per sequence) through the block table.
+
+    q [S, Hq, hd]; pools [NB, bs, Hkv, hd] (K may be uint8 q8_0 [NB, bs, row_bytes]);
+    block_table int32 [S, MB]; seq_lens int32 [S]; window int32 [S, 2] (span) or
+    [S, n_runs, 2] (kv_map).  Returns (out float32 [S, Hq, hd], lse float32 [S, Hq]).
+    part = "partials" / "merge" runs one of the two passes (same workspace)."""
+    torch = _torch()
+    S = q.shape[0]
+    shape = make_shape(q, k_pool, v_pool, block_table, S, scale, flags, split_tokens)
+    _i32(seq_lens, "seq_lens")
+    m, n_runs, win = _window_args(mode, window)
+    need = int(lib().pkv_decode_workspace_bytes(ctypes.byref(shape), m, n_runs))
+    if need == 0:
+        _check(lib().pkv_paged_attn_decode(ctypes.byref(shape), None, None, None, None, None, m, n_runs,
+                                           None, None, None, None, 0, None))
+    ws = _workspace(need, q, workspace)
+    if out is None:
+        out = torch.empty((S, shape.n_q_heads, shape.head_dim), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((S, shape.n_q_heads), dtype=torch.float32, device=q.device)
+    st = _stream(q)
+    L = lib()
+    if part == "both":
+        _check(L.pkv_paged_attn_decode(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(block_table), _ptr(seq_lens), m, n_runs, _ptr(win),
+                                       _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st))
+    elif part == "partials":
+        _check(L.pkv_paged_attn_decode_partials(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                                _ptr(block_table), _ptr(seq_lens), m, n_runs, _ptr(win),
+                                                _ptr(ws), ws.numel(), st))
+    elif part == "merge":
+        _check(L.pkv_paged_attn_decode_merge(ctypes.byref(shape), _ptr(seq_lens), m, n_runs, _ptr(win),
+                                             _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st))
+    else:
+        raise ValueError(part)
+    return out, lse
+
+
+def prefill_workspace_bytes(shape: Shape, n_q_total: int, max_q_per_seq: int, mode: str = "kv_map",
+                            n_runs: int = 1) -> int:
+    return int(lib().pkv_prefill_workspace_bytes(ctypes.byref(shape), n_q_total, max_q_per_seq,
+                                                 MODES[mode], n_runs))
+
+
+def paged_attn_prefill_window(q, cu_q, q_pos, k_pool, v_pool, block_table, seq_lens, scale: float,
+                              max_q_per_seq: int, mode: str = "kv_map", window=None, out=None, lse=None,
+                              workspace=None, flags: int = 0):
+    """Windowed prefill: queries of sequence s are rows cu_q[s]..cu_q[s+1]-1 of q
+    [Nq, Hq, hd] at positions q_pos [Nq].  Returns (out [Nq, Hq, hd], lse [Nq, Hq])."""
+    torch = _torch()
+    S = block_table.shape[0]
+    Nq = q.shape[0]
+    shape = make_shape(q, k_pool, v_pool, block_table, S, scale, flags)
+    for name, t in (("cu_q", cu_q), ("q_pos", q_pos), ("seq_lens", seq_lens)):
+        _i32(t, name)
+    m, n_runs, win = _window_args(mode, window)
+    need = int(lib().pkv_prefill_workspace_bytes(ctypes.byref(shape), Nq, max_q_per_seq, m, n_runs))
+    ws = _workspace(need, q, workspace) if need else workspace
+    if out is None:
+        out = torch.empty((Nq, shape.n_q_heads, shape.head_dim), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((Nq, shape.n_q_heads), dtype=torch.float32, device=q.device)
+    _check(lib().pkv_paged_attn_prefill_window(
+        ctypes.byref(shape), Nq, max_q_per_seq, _ptr(q), _ptr(cu_q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), _ptr(seq_lens), m, n_runs, _ptr(win), _ptr(out), _ptr(lse), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(q)))
+    return out, lse
+
+
+def resolve_rows(block_table, seq_lens, block_size: int, n_kv_heads: int, head_dim: int, n_pool_blocks: int,
+                 n_cand: int, mode: str = "causal", window=None, cu_q=None, q_pos=None, n_q_heads=None,
+                 k_fmt: int = F16, v_fmt: int = F16, q_fmt: int = F16):
+    """Pool row read by every (query, window candidate), or -1 (debug export)."""
+    torch = _torch()
+    S = block_table.shape[0]
+    shape = Shape(n_seqs=S, n_q_heads=n_q_heads or n_kv_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
+                  block_size=block_size, n_pool_blocks=n_pool_blocks, max_blocks_per_seq=block_table.shape[1],
+                  q_fmt=q_fmt, k_fmt=k_fmt, v_fmt=v_fmt, scale=1.0, flags=0, split_tokens=0)
+    m, n_runs, win = _window_args(mode, window)
+    nq = S if cu_q is None else q_pos.shape[0]
+    rows = torch.empty((nq, n_cand), dtype=torch.int32, device=block_table.device)
+    _check(lib().pkv_resolve_rows(ctypes.byref(shape), nq, _ptr(cu_q), _ptr(q_pos), _ptr(block_table),
+                                  _ptr(seq_lens), m, n_runs, _ptr(win), n_cand, _ptr(rows),
+                                  _stream(block_table)))
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# moves
+
+
+def order_moves(moves) -> list:
+    """Application order of (src, dst, len) moves (host call)."""
+    import numpy as np
+
+    mv = np.ascontiguousarray(np.asarray(moves, dtype=np.int32).reshape(-1, 3))
+    n = mv.shape[0]
+    order = np.zeros(max(n, 1), dtype=np.int32)
+    n_out = ctypes.c_int32(0)
+    _check(lib().pkv_order_moves(mv.ctypes.data, n, order.ctypes.data, ctypes.byref(n_out)))
+    return order[: n_out.value].tolist()
+
+
+def kv_copy_cells(k_pool, v_pool, moves, workspace=None):
+    """Apply (src, dst, len) row moves (host int32 array [n, 3]) to both pools
+    in order_moves order, bit-exact; pools are viewed as rows (first two axes)."""
+    import numpy as np
+
+    torch = _torch()
+    mv = np.ascontiguousarray(np.asarray(moves, dtype=np.int32).reshape(-1, 3))
+    n = mv.shape[0]
+    n_rows = k_pool.shape[0] * k_pool.shape[1]
+    rbk = k_pool.numel() * k_pool.element_size() // n_rows
+    rbv = 0
+    if v_pool is not None:
+        if v_pool.shape[0] * v_pool.shape[1] != n_rows:
+            raise ValueError("K and V pools must have the same number of rows")
+        rbv = v_pool.numel() * v_pool.element_size() // n_rows
+    for t in (k_pool, v_pool):
+        if t is not None and not t.is_contiguous():
+            raise TypeError("pools must be contiguous")
+    need = int(lib().pkv_copy_cells_workspace_bytes(mv.ctypes.data, n, rbk, max(rbv, 0)))
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=k_pool.device)
+    _check(lib().pkv_kv_copy_cells(_ptr(k_pool), _ptr(v_pool), n_rows, rbk, rbv, mv.ctypes.data, n,
+                                   _ptr(ws), ws.numel(), _stream(k_pool)))
+    return k_pool, v_pool

@@ -1,0 +1,26 @@
+// Decode kernel instances for the (q, K, V) format combination kComboF16.
+#include "decode_impl.hpp"
+
+namespace pkv {
+
+hipError_t launch_decode_split_f16(const AttnArgs& a, int hd, int bs, int g, hipStream_t st,
+                                     bool* found) {
+  const dim3 grid(a.n_runs * a.nspl, a.n_kv_heads, a.n_seqs);
+#define PKV_CASE(HD, BS, G)                                                                \
+  if (hd == HD && bs == BS && g == G) {                                                    \
+    hipLaunchKernelGGL((decode_split_kernel<HD, BS, G, kComboF16>), grid, dim3(64), 0, st, a); \
+    *found = true;                                                                         \
+    return hipGetLastError();                                                              \
+  }
+#define PKV_CASES_G(HD, BS) PKV_CASE(HD, BS, 1) PKV_CASE(HD, BS, 2) PKV_CASE(HD, BS, 3) PKV_CASE(HD, BS, 4) PKV_CASE(HD, BS, 8)
+  PKV_CASES_G(64, 16)
+  PKV_CASES_G(128, 16)
+  PKV_CASES_G(256, 16)
+  PKV_CASES_G(128, 32)
+#undef PKV_CASES_G
+#undef PKV_CASE
+  *found = false;
+  return hipSuccess;
+}
+
+}  // namespace pkv

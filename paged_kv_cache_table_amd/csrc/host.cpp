@@ -1,0 +1,545 @@
+// C ABI of the paged-attention library: argument validation, dispatch over
+// (head_dim, block_size, group, formats), split planning, order_moves and
+// the copy_cells plan.  Every host-checkable condition is checked before
+// the first launch, so a refused call leaves outputs and pools untouched.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pkv_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_err.clear();
+  return PKV_OK;
+}
+
+const char* fmt_name(int f) {
+  switch (f) {
+    case PKV_F32: return "f32";
+    case PKV_F16: return "f16";
+    case PKV_Q8_0: return "q8_0";
+    default: return "?";
+  }
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t row_bytes_of(int fmt, int hkv, int hd) {
+  if (hkv <= 0 || hd <= 0) return 0;
+  switch (fmt) {
+    case PKV_F32: return 4ll * hkv * hd;
+    case PKV_F16: return 2ll * hkv * hd;
+    case PKV_Q8_0: {
+      if (hd % 32) return 0;
+      const int64_t raw = (int64_t)hkv * (hd / 32) * 34;
+      return (raw + 3) / 4 * 4;
+    }
+    default: return 0;
+  }
+}
+
+bool supported_head_block(int hd, int bs) {
+  return (hd == 64 && bs == 16) || (hd == 128 && bs == 16) || (hd == 256 && bs == 16) ||
+         (hd == 128 && bs == 32);
+}
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 3 || g == 4 || g == 8; }
+
+// Format combination index, or -1.
+int combo_of(int qf, int kf, int vf) {
+  if (qf == PKV_F32 && kf == PKV_F32 && vf == PKV_F32) return pkv::kComboF32;
+  if (qf == PKV_F16 && kf == PKV_F16 && vf == PKV_F16) return pkv::kComboF16;
+  if (qf == PKV_F16 && kf == PKV_Q8_0 && vf == PKV_F16) return pkv::kComboQ8H;
+  if (qf == PKV_F32 && kf == PKV_Q8_0 && vf == PKV_F32) return pkv::kComboQ8F;
+  return -1;
+}
+
+struct Plan {
+  int combo = -1, g = 0, runs = 1, split = 0, nspl = 0;
+  size_t off_o = 0, off_ml = 0, off_err = 0, total = 0;
+};
+
+// Validation shared by every attention call.
+pkv_status check_attn(const pkv_shape* sh, int mode, int n_runs, const void* window, Plan* P) {
+  if (!sh) return fail(PKV_E_ARG, "shape is NULL");
+  if (sh->n_seqs < 0 || sh->n_seqs > 65535)
+    return fail(PKV_E_ARG, "n_seqs %d outside [0, 65535]", sh->n_seqs);
+  if (sh->n_q_heads <= 0 || sh->n_kv_heads <= 0 || sh->n_kv_heads > 65535)
+    return fail(PKV_E_ARG, "head counts must be positive (n_q_heads %d, n_kv_heads %d)",
+                sh->n_q_heads, sh->n_kv_heads);
+  if (sh->n_q_heads % sh->n_kv_heads)
+    return fail(PKV_E_ARG, "n_q_heads %d is not a multiple of n_kv_heads %d", sh->n_q_heads,
+                sh->n_kv_heads);
+  if (sh->head_dim <= 0 || sh->block_size <= 0)
+    return fail(PKV_E_ARG, "head_dim %d and block_size %d must be positive", sh->head_dim,
+                sh->block_size);
+  if (sh->n_pool_blocks <= 0 || sh->max_blocks_per_seq <= 0)
+    return fail(PKV_E_ARG, "n_pool_blocks %d and max_blocks_per_seq %d must be positive",
+                sh->n_pool_blocks, sh->max_blocks_per_seq);
+  if ((int64_t)sh->max_blocks_per_seq * sh->block_size > INT32_MAX)
+    return fail(PKV_E_ARG, "max_blocks_per_seq * block_size overflows int32");
+  for (int f : {sh->q_fmt, sh->k_fmt, sh->v_fmt})
+    if (f != PKV_F32 && f != PKV_F16 && f != PKV_Q8_0)
+      return fail(PKV_E_ARG, "unknown KV format value %d", f);
+  if (!std::isfinite(sh->scale)) return fail(PKV_E_ARG, "scale is not finite");
+  if (mode != PKV_WIN_CAUSAL && mode != PKV_WIN_SPAN && mode != PKV_WIN_KV_MAP)
+    return fail(PKV_E_ARG, "unknown window mode %d", mode);
+  if (mode == PKV_WIN_KV_MAP && (n_runs < 1 || n_runs > PKV_KV_MAP_MAX_SPANS))
+    return fail(PKV_E_ARG, "kv_map needs 1..%d runs per sequence, got %d", PKV_KV_MAP_MAX_SPANS,
+                n_runs);
+  if (mode != PKV_WIN_CAUSAL && !window && sh->n_seqs > 0)
+    return fail(PKV_E_ARG, "window mode %d needs a window input", mode);
+  const int g = sh->n_q_heads / sh->n_kv_heads;
+  if (!supported_head_block(sh->head_dim, sh->block_size))
+    return fail(PKV_E_UNSUPPORTED,
+                "unsupported (head_dim, block_size) = (%d, %d): supported are (64,16), (128,16), "
+                "(256,16), (128,32)",
+                sh->head_dim, sh->block_size);
+  if (!supported_group(g))
+    return fail(PKV_E_UNSUPPORTED, "unsupported GQA group %d (n_q_heads %d / n_kv_heads %d)", g,
+                sh->n_q_heads, sh->n_kv_heads);
+  const int combo = combo_of(sh->q_fmt, sh->k_fmt, sh->v_fmt);
+  if (combo < 0)
+    return fail(PKV_E_UNSUPPORTED,
+                "unsupported (q, K, V) formats (%s, %s, %s): supported are (f32,f32,f32), "
+                "(f16,f16,f16), (f16,q8_0,f16), (f32,q8_0,f32)",
+                fmt_name(sh->q_fmt), fmt_name(sh->k_fmt), fmt_name(sh->v_fmt));
+  P->combo = combo;
+  P->g = g;
+  P->runs = mode == PKV_WIN_KV_MAP ? n_runs : 1;
+  return PKV_OK;
+}
+
+// Decode split size: the largest of 64, 32, 16, 8, 4 blocks that still gives
+// enough work items (an upper bound from the table width) to spread over the
+// GPU with a short tail.  Depends on the shape only.
+int auto_split(const pkv_shape* sh, int runs) {
+  const int64_t ctx = (int64_t)sh->max_blocks_per_seq * sh->block_size;
+  const int64_t target = 32768;
+  for (int nb : {64, 32, 16, 8}) {
+    const int64_t sp = (int64_t)nb * sh->block_size;
+    const int64_t items = (int64_t)sh->n_seqs * sh->n_kv_heads * runs * ((ctx + sp - 1) / sp);
+    if (items >= target) return (int)sp;
+  }
+  return 4 * sh->block_size;
+}
+
+pkv_status plan_decode(const pkv_shape* sh, int mode, int n_runs, const void* window, Plan* P) {
+  pkv_status st = check_attn(sh, mode, n_runs, window, P);
+  if (st) return st;
+  int split = sh->split_tokens;
+  if (split == 0) {
+    split = auto_split(sh, P->runs);
+  } else if (split < 0 || split % sh->block_size || split > 64 * sh->block_size) {
+    return fail(PKV_E_ARG, "split_tokens %d must be a positive multiple of block_size %d, at most 64 blocks",
+                split, sh->block_size);
+  }
+  const int64_t ctx = (int64_t)sh->max_blocks_per_seq * sh->block_size;
+  const int64_t nspl = (ctx + split - 1) / split;
+  if (nspl * P->runs > INT32_MAX / 2) return fail(PKV_E_ARG, "too many split slots");
+  P->split = split;
+  P->nspl = (int)nspl;
+  const size_t slots = (size_t)sh->n_seqs * nspl * P->runs * sh->n_q_heads;
+  P->off_o = 0;
+  P->off_ml = align_up(slots * sh->head_dim * sizeof(float), 256);
+  P->off_err = P->off_ml + align_up(slots * 2 * sizeof(float), 256);
+  P->total = P->off_err + 256;
+  return PKV_OK;
+}
+
+pkv::AttnArgs base_args(const pkv_shape* sh, const Plan& P) {
+  pkv::AttnArgs a{};
+  a.n_seqs = sh->n_seqs;
+  a.n_q_heads = sh->n_q_heads;
+  a.n_kv_heads = sh->n_kv_heads;
+  a.n_pool_blocks = sh->n_pool_blocks;
+  a.max_blocks = sh->max_blocks_per_seq;
+  a.block_size = sh->block_size;
+  a.k_row_bytes = row_bytes_of(sh->k_fmt, sh->n_kv_heads, sh->head_dim);
+  a.v_row_bytes = row_bytes_of(sh->v_fmt, sh->n_kv_heads, sh->head_dim);
+  a.score_mul = (float)((double)sh->scale * 1.4426950408889634);
+  a.flags = sh->flags;
+  a.n_runs = P.runs;
+  a.split = P.split;
+  a.nspl = P.nspl;
+  return a;
+}
+
+pkv_status device_fail(hipError_t e, const char* what) {
+  return fail(PKV_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+pkv_status finish_checked(const pkv::AttnArgs& a, hipStream_t st) {
+  if (!(a.flags & PKV_FLAG_CHECKED)) return ok();
+  int32_t bad = 0;
+  hipError_t e = hipMemcpyAsync(&bad, a.err, sizeof bad, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_fail(e, "reading the checked-mode error word");
+  if (bad)
+    return fail(PKV_E_ARG,
+                "%d block-table entries are outside [-1, n_pool_blocks); they were read as holes",
+                bad);
+  return ok();
+}
+
+enum DecodePart { kBoth, kPartials, kMerge };
+
+pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t mode, int32_t n_runs, const int32_t* window, float* out, float* lse,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Plan P;
+  pkv_status st = plan_decode(sh, mode, n_runs, window, &P);
+  if (st) return st;
+  if (sh->n_seqs == 0) return ok();
+  if (!seq_lens) return fail(PKV_E_ARG, "seq_lens is NULL");
+  if (part != kMerge && (!q || !k_pool || !v_pool || !block_table))
+    return fail(PKV_E_ARG, "q, k_pool, v_pool and block_table must be non-NULL");
+  if (part != kPartials && !out) return fail(PKV_E_ARG, "out is NULL");
+  if (!ws || ws_bytes < P.total)
+    return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws ? ws_bytes : (size_t)0, P.total);
+  if (((uintptr_t)ws) % 256) return fail(PKV_E_WORKSPACE, "workspace must be 256-byte aligned");
+  pkv::AttnArgs a = base_args(sh, P);
+  a.q = q;
+  a.k_pool = (const unsigned char*)k_pool;
+  a.v_pool = (const unsigned char*)v_pool;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.window = window;
+  a.mode = mode;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = (float*)((char*)ws + P.off_o);
+  a.part_ml = (float*)((char*)ws + P.off_ml);
+  a.err = (int32_t*)((char*)ws + P.off_err);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (part != kMerge) {
+    if (a.flags & PKV_FLAG_CHECKED) {
+      e = pkv::launch_zero_words(a.err, 1, s);
+      if (e != hipSuccess) return device_fail(e, "clearing the error word");
+    }
+    bool found = false;
+    e = pkv::launch_decode_split(a, P.combo, sh->head_dim, sh->block_size, P.g, s, &found);
+    if (!found)
+      return fail(PKV_E_UNSUPPORTED, "no decode kernel for head_dim %d block %d group %d",
+                  sh->head_dim, sh->block_size, P.g);
+    if (e != hipSuccess) return device_fail(e, "decode split launch");
+  }
+  if (part != kPartials) {
+    e = pkv::launch_decode_merge(a, sh->head_dim, s);
+    if (e != hipSuccess) return device_fail(e, "decode merge launch");
+  }
+  if (part != kMerge) return finish_checked(a, s);
+  return ok();
+}
+
+// order_moves: indices of the effective moves, upward moves (dst > src) by
+// descending src then descending dst, then downward moves by ascending src
+// then ascending dst; ties by input index.
+std::vector<int32_t> order_moves_impl(const int32_t* mv, int32_t n) {
+  std::vector<int32_t> up, down;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = mv[3 * i], d = mv[3 * i + 1], len = mv[3 * i + 2];
+    if (len <= 0 || d == s) continue;
+    (d > s ? up : down).push_back(i);
+  }
+  std::stable_sort(up.begin(), up.end(), [&](int32_t a, int32_t b) {
+    if (mv[3 * a] != mv[3 * b]) return mv[3 * a] > mv[3 * b];
+    return mv[3 * a + 1] > mv[3 * b + 1];
+  });
+  std::stable_sort(down.begin(), down.end(), [&](int32_t a, int32_t b) {
+    if (mv[3 * a] != mv[3 * b]) return mv[3 * a] < mv[3 * b];
+    return mv[3 * a + 1] < mv[3 * b + 1];
+  });
+  up.insert(up.end(), down.begin(), down.end());
+  return up;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t pkv_row_bytes(int32_t fmt, int32_t n_kv_heads, int32_t head_dim) {
+  return row_bytes_of(fmt, n_kv_heads, head_dim);
+}
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+size_t pkv_decode_workspace_bytes(const pkv_shape* shape, int32_t mode, int32_t n_runs) {
+  Plan P;
+  static const int32_t dummy[2] = {0, 0};
+  if (plan_decode(shape, mode, n_runs, mode == PKV_WIN_CAUSAL ? nullptr : dummy, &P)) return 0;
+  return P.total;
+}
+
+int32_t pkv_decode_split_tokens(const pkv_shape* shape, int32_t mode, int32_t n_runs) {
+  Plan P;
+  static const int32_t dummy[2] = {0, 0};
+  if (plan_decode(shape, mode, n_runs, mode == PKV_WIN_CAUSAL ? nullptr : dummy, &P)) return 0;
+  return P.split;
+}
+
+pkv_status pkv_paged_attn_decode(const pkv_shape* shape, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t mode, int32_t n_runs,
+                                 const int32_t* window, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return decode_impl(kBoth, shape, q, k_pool, v_pool, block_table, seq_lens, mode, n_runs, window,
+                     out, lse, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attn_decode_partials(const pkv_shape* shape, const void* q,
+                                          const void* k_pool, const void* v_pool,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          int32_t mode, int32_t n_runs, const int32_t* window,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kPartials, shape, q, k_pool, v_pool, block_table, seq_lens, mode, n_runs,
+                     window, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attn_decode_merge(const pkv_shape* shape, const int32_t* seq_lens,
+                                       int32_t mode, int32_t n_runs, const int32_t* window,
+                                       float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return decode_impl(kMerge, shape, nullptr, nullptr, nullptr, nullptr, seq_lens, mode, n_runs,
+                     window, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t pkv_prefill_workspace_bytes(const pkv_shape* shape, int32_t n_q_total,
+                                   int32_t max_q_per_seq, int32_t mode, int32_t n_runs) {
+  Plan P;
+  static const int32_t dummy[2] = {0, 0};
+  if (check_attn(shape, mode, n_runs, mode == PKV_WIN_CAUSAL ? nullptr : dummy, &P)) return 0;
+  if (n_q_total < 0 || max_q_per_seq < 0) return 0;
+  pkv::AttnArgs a = base_args(shape, P);
+  a.mode = mode;
+  a.n_q_total = n_q_total;
+  a.max_q = max_q_per_seq;
+  bool found = false;
+  const size_t need = pkv::prefill_workspace(a, P.combo, shape->head_dim, shape->block_size, P.g, &found);
+  return found ? need : 0;
+}
+
+pkv_status pkv_paged_attn_prefill_window(const pkv_shape* sh, int32_t n_q_total,
+                                         int32_t max_q_per_seq, const void* q,
+                                         const int32_t* cu_q, const int32_t* q_pos,
+                                         const void* k_pool, const void* v_pool,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         int32_t mode, int32_t n_runs, const int32_t* window,
+                                         float* out, float* lse, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  Plan P;
+  pkv_status st = check_attn(sh, mode, n_runs, window, &P);
+  if (st) return st;
+  if (n_q_total < 0 || max_q_per_seq < 0)
+    return fail(PKV_E_ARG, "n_q_total %d and max_q_per_seq %d must be >= 0", n_q_total,
+                max_q_per_seq);
+  if (sh->n_seqs == 0 || n_q_total == 0 || max_q_per_seq == 0) return ok();
+  if (!q || !cu_q || !q_pos || !k_pool || !v_pool || !block_table || !seq_lens || !out)
+    return fail(PKV_E_ARG, "prefill inputs and out must be non-NULL");
+  pkv::AttnArgs a = base_args(sh, P);
+  a.q = q;
+  a.cu_q = cu_q;
+  a.q_pos = q_pos;
+  a.k_pool = (const unsigned char*)k_pool;
+  a.v_pool = (const unsigned char*)v_pool;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.window = window;
+  a.mode = mode;
+  a.out = out;
+  a.lse = lse;
+  a.n_q_total = n_q_total;
+  a.max_q = max_q_per_seq;
+  bool found = false;
+  const size_t need = pkv::prefill_workspace(a, P.combo, sh->head_dim, sh->block_size, P.g, &found);
+  if (!found)
+    return fail(PKV_E_UNSUPPORTED, "no prefill kernel for head_dim %d block %d group %d formats (%s, %s, %s)",
+                sh->head_dim, sh->block_size, P.g, fmt_name(sh->q_fmt), fmt_name(sh->k_fmt),
+                fmt_name(sh->v_fmt));
+  if (need && (!ws || ws_bytes < need))
+    return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws ? ws_bytes : (size_t)0, need);
+  if (need && ((uintptr_t)ws) % 256) return fail(PKV_E_WORKSPACE, "workspace must be 256-byte aligned");
+  a.part_o = (float*)ws;
+  a.err = need ? (int32_t*)((char*)ws + need - 256) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  if ((a.flags & PKV_FLAG_CHECKED) && a.err) {
+    hipError_t e = pkv::launch_zero_words(a.err, 1, s);
+    if (e != hipSuccess) return device_fail(e, "clearing the error word");
+  } else {
+    a.flags &= ~PKV_FLAG_CHECKED;
+  }
+  hipError_t e = pkv::launch_prefill(a, P.combo, sh->head_dim, sh->block_size, P.g, s, &found);
+  if (e != hipSuccess) return device_fail(e, "prefill launch");
+  return finish_checked(a, s);
+}
+
+pkv_status pkv_order_moves(const int32_t* moves, int32_t n, int32_t* order_out, int32_t* n_out) {
+  if (n < 0) return fail(PKV_E_ARG, "negative move count %d", n);
+  if (n > 0 && (!moves || !order_out)) return fail(PKV_E_ARG, "moves and order_out must be non-NULL");
+  if (!n_out) return fail(PKV_E_ARG, "n_out is NULL");
+  std::vector<int32_t> o = order_moves_impl(moves, n);
+  std::copy(o.begin(), o.end(), order_out);
+  *n_out = (int32_t)o.size();
+  return ok();
+}
+
+size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t row_bytes_k,
+                                      int64_t row_bytes_v) {
+  if (n < 0 || (n > 0 && !moves) || row_bytes_k <= 0 || row_bytes_v < 0) return 0;
+  int64_t rows = 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (moves[3 * i + 2] > 0 && moves[3 * i] != moves[3 * i + 1]) rows += moves[3 * i + 2];
+  return align_up((size_t)rows * 2 * sizeof(int32_t) * 2, 256) +
+         align_up((size_t)rows * (size_t)row_bytes_k, 256) +
+         align_up((size_t)rows * (size_t)row_bytes_v, 256) + 256;
+}
+
+pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int64_t n_pool_rows, int64_t row_bytes_k,
+                             int64_t row_bytes_v, const int32_t* moves, int32_t n, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!k_pool) return fail(PKV_E_ARG, "k_pool is NULL");
+  if (n < 0) return fail(PKV_E_ARG, "negative move count %d", n);
+  if (n > 0 && !moves) return fail(PKV_E_ARG, "moves is NULL");
+  if (n_pool_rows <= 0 || n_pool_rows > INT32_MAX)
+    return fail(PKV_E_ARG, "n_pool_rows %lld outside [1, 2^31)", (long long)n_pool_rows);
+  if (row_bytes_k <= 0 || row_bytes_k % 4)
+    return fail(PKV_E_ARG, "row_bytes_k %lld must be a positive multiple of 4", (long long)row_bytes_k);
+  if (v_pool && (row_bytes_v <= 0 || row_bytes_v % 4))
+    return fail(PKV_E_ARG, "row_bytes_v %lld must be a positive multiple of 4", (long long)row_bytes_v);
+  int64_t lo = INT64_MAX, hi = -1;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t s = moves[3 * i], d = moves[3 * i + 1], len = moves[3 * i + 2];
+    if (len <= 0 || s == d) continue;
+    if (s < 0 || d < 0 || s + len > n_pool_rows || d + len > n_pool_rows)
+      return fail(PKV_E_ARG, "move %d (src %lld, dst %lld, len %lld) leaves [0, %lld)", i,
+                  (long long)s, (long long)d, (long long)len, (long long)n_pool_rows);
+    lo = std::min(lo, std::min(s, d));
+    hi = std::max(hi, std::max(s, d) + len);
+  }
+  const std::vector<int32_t> order = order_moves_impl(moves, n);
+  if (order.empty()) return ok();
+  // Final source of every row of [lo, hi) after the ordered memmoves.
+  std::vector<int32_t> prov(hi - lo);
+  for (int64_t r = lo; r < hi; ++r) prov[r - lo] = (int32_t)r;
+  for (int32_t i : order) {
+    const int64_t s = moves[3 * i], d = moves[3 * i + 1], len = moves[3 * i + 2];
+    std::memmove(&prov[d - lo], &prov[s - lo], (size_t)len * sizeof(int32_t));
+  }
+  std::vector<char> changed(hi - lo, 0);
+  int64_t n_changed = 0;
+  for (int64_t r = lo; r < hi; ++r)
+    if (prov[r - lo] != r) {
+      changed[r - lo] = 1;
+      ++n_changed;
+    }
+  // Rows read from a row that is also written go through the stage.
+  std::vector<int32_t> stage_of(hi - lo, -1);
+  std::vector<int32_t> gather, scatter;
+  gather.reserve(2 * n_changed);
+  scatter.reserve(2 * n_changed);
+  int32_t n_stage = 0;
+  for (int64_t r = lo; r < hi; ++r) {
+    if (!changed[r - lo]) continue;
+    const int32_t src = prov[r - lo];
+    int32_t y = src;
+    if (changed[src - lo]) {
+      if (stage_of[src - lo] < 0) {
+        stage_of[src - lo] = n_stage++;
+        gather.push_back(src);
+        gather.push_back(stage_of[src - lo]);
+      }
+      y = -(stage_of[src - lo] + 1);
+    }
+    scatter.push_back((int32_t)r);
+    scatter.push_back(y);
+  }
+  const size_t idx_bytes = align_up((gather.size() + scatter.size()) * sizeof(int32_t), 256);
+  const size_t stage_k = align_up((size_t)n_stage * (size_t)row_bytes_k, 256);
+  const size_t stage_v = v_pool ? align_up((size_t)n_stage * (size_t)row_bytes_v, 256) : 0;
+  const size_t need = idx_bytes + stage_k + stage_v;
+  if (!ws || ws_bytes < need)
+    return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws ? ws_bytes : (size_t)0, need);
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> idx(gather);
+  idx.insert(idx.end(), scatter.begin(), scatter.end());
+  int32_t* d_idx = (int32_t*)ws;
+  unsigned char* stage = (unsigned char*)ws + idx_bytes;
+  hipError_t e = hipMemcpyAsync(d_idx, idx.data(), idx.size() * sizeof(int32_t),
+                                hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_fail(e, "uploading the move plan");
+  const int32_t n_gather = (int32_t)(gather.size() / 2), n_scatter = (int32_t)(scatter.size() / 2);
+  const int32_t* d_gather = d_idx;
+  const int32_t* d_scatter = d_idx + gather.size();
+  struct Pool { unsigned char* p; int64_t rb; size_t off; } pools[2] = {
+      {(unsigned char*)k_pool, row_bytes_k, 0}, {(unsigned char*)v_pool, row_bytes_v, stage_k}};
+  for (const Pool& pl : pools) {
+    if (!pl.p) continue;
+    e = pkv::launch_copy_rows(1, pl.p, stage, pl.rb, d_gather, n_gather, (int64_t)pl.off, pl.rb, s);
+    if (e != hipSuccess) return device_fail(e, "copy_cells gather launch");
+  }
+  for (const Pool& pl : pools) {
+    if (!pl.p) continue;
+    e = pkv::launch_copy_rows(2, pl.p, stage, pl.rb, d_scatter, n_scatter, (int64_t)pl.off, pl.rb, s);
+    if (e != hipSuccess) return device_fail(e, "copy_cells scatter launch");
+  }
+  return ok();
+}
+
+pkv_status pkv_resolve_rows(const pkv_shape* sh, int32_t n_q_total, const int32_t* cu_q,
+                            const int32_t* q_pos, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t mode, int32_t n_runs,
+                            const int32_t* window, int32_t n_cand, int32_t* rows_out,
+                            void* stream) {
+  Plan P;
+  pkv_status st = check_attn(sh, mode, n_runs, window, &P);
+  if (st) return st;
+  if (n_q_total < 0 || n_cand < 0) return fail(PKV_E_ARG, "negative n_q_total or n_cand");
+  if ((cu_q == nullptr) != (q_pos == nullptr))
+    return fail(PKV_E_ARG, "cu_q and q_pos must both be given (prefill) or both be NULL (decode)");
+  if (!cu_q && n_q_total != sh->n_seqs)
+    return fail(PKV_E_ARG, "decode resolve needs n_q_total == n_seqs (%d != %d)", n_q_total,
+                sh->n_seqs);
+  if (n_q_total == 0 || n_cand == 0) return ok();
+  if (n_q_total > 65535) return fail(PKV_E_ARG, "n_q_total %d above 65535", n_q_total);
+  if (!block_table || !seq_lens || !rows_out) return fail(PKV_E_ARG, "NULL input");
+  pkv::AttnArgs a = base_args(sh, P);
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.window = window;
+  a.mode = mode;
+  a.cu_q = cu_q;
+  a.q_pos = q_pos;
+  a.n_q_total = n_q_total;
+  a.flags &= ~PKV_FLAG_CHECKED;
+  hipError_t e = pkv::launch_resolve(a, sh->block_size, n_cand, rows_out, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "resolve launch");
+  return ok();
+}
+
+}  // extern "C"

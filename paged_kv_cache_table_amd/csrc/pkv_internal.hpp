@@ -1,0 +1,199 @@
+// Internal declarations shared by the host layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Format combinations (q, K, V) the kernels are built for.
+enum Combo : int { kComboF32 = 0, kComboF16 = 1, kComboQ8H = 2, kComboQ8F = 3, kNumCombos = 4 };
+
+// Everything an attention kernel reads, flattened into one by-value struct.
+struct AttnArgs {
+  const void* q;
+  const unsigned char* k_pool;
+  const unsigned char* v_pool;
+  const int32_t* table;     // [n_seqs][max_blocks]
+  const int32_t* seq_lens;  // [n_seqs]
+  const int32_t* window;    // span [S][2] | kv_map [S][n_runs][2] | null
+  const int32_t* cu_q;      // prefill [S+1]
+  const int32_t* q_pos;     // prefill [n_q_total]
+  float* out;
+  float* lse;
+  float* part_o;   // decode partials [S][n_slots][Hq][HD]
+  float* part_ml;  // decode partials [S][n_slots][Hq][2] = (max, sum)
+  int32_t* err;    // checked mode: count of bad block ids
+  int32_t n_seqs, n_q_heads, n_kv_heads, n_pool_blocks, max_blocks, block_size;
+  int32_t mode, n_runs;  // n_runs = runs per sequence (1 unless kv_map)
+  int32_t split, nspl;   // decode: tokens per split, split slots per run
+  int32_t n_q_total, max_q;
+  int64_t k_row_bytes, v_row_bytes;
+  float score_mul;  // scale * log2(e): scores are kept in the log2 domain
+  uint32_t flags;
+};
+
+// ---------------------------------------------------------------------------
+// Window geometry, shared by the split kernel, the merge and the resolver so
+// that all of them agree on which work items exist.
+
+__host__ __device__ inline int32_t clamp_seq_len(int32_t L, int32_t max_blocks, int32_t bs) {
+  int64_t cap = (int64_t)max_blocks * bs;
+  if (L < 0) return 0;
+  return (int64_t)L > cap ? (int32_t)cap : L;
+}
+
+// Run r of sequence s as a half-open range of positions, clipped to
+// [0, limit).  Causal is one run [0, limit); a span is one run [lo, hi); a
+// kv_map run (cell, len) is [cell, cell + len), unused when len <= 0.
+__device__ inline void run_range(const AttnArgs& a, int s, int r, int32_t limit, int32_t& lo,
+                                 int32_t& hi) {
+  int64_t x0 = 0, x1 = 0;
+  if (a.mode == PKV_WIN_CAUSAL) {
+    x0 = 0;
+    x1 = limit;
+  } else if (a.mode == PKV_WIN_SPAN) {
+    x0 = a.window[2 * s];
+    x1 = a.window[2 * s + 1];
+  } else {
+    const int32_t* w = a.window + ((int64_t)s * a.n_runs + r) * 2;
+    int64_t c = w[0], n = w[1];
+    if (n > 0) {
+      x0 = c;
+      x1 = c + n;
+    }
+  }
+  if (x0 < 0) x0 = 0;
+  if (x1 > limit) x1 = limit;
+  if (x1 < x0) x1 = x0;
+  lo = (int32_t)x0;
+  hi = (int32_t)x1;
+}
+
+// Positions a decode split slot covers: [lo, hi) of run r intersected with
+// the aligned split window [k*split, (k+1)*split).  Empty => no work item.
+__device__ inline void split_range(const AttnArgs& a, int s, int slot, int32_t limit, int32_t& lo,
+                                   int32_t& hi) {
+  int r = slot / a.nspl;
+  int k = slot - r * a.nspl;
+  int32_t rl, rh;
+  run_range(a, s, r, limit, rl, rh);
+  int64_t w0 = (int64_t)k * a.split, w1 = w0 + a.split;
+  int64_t x0 = rl > w0 ? rl : w0;
+  int64_t x1 = rh < w1 ? rh : w1;
+  if (x1 < x0) x1 = x0;
+  lo = (int32_t)x0;
+  hi = (int32_t)x1;
+}
+
+// Physical block of logical block b, or -1 for a hole; ids outside
+// [0, n_pool_blocks) count as holes (and, in checked mode, are counted by
+// the one reader that passes count = true).
+__device__ inline int32_t block_id(const AttnArgs& a, int s, int32_t b, bool count = false) {
+  int32_t id = a.table[(int64_t)s * a.max_blocks + b];
+  if (id < 0 || id >= a.n_pool_blocks) {
+    if (count && id != PKV_INVALID_BLOCK_ID && (a.flags & PKV_FLAG_CHECKED) && a.err)
+      atomicAdd(a.err, 1);
+    return -1;
+  }
+  return id;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers.  DPP controls (GFX9 encoding): quad_perm selectors,
+// row_ror:n = 0x120 + n, row_half_mirror = 0x141.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppRor4 = 0x124;
+constexpr int kDppRor8 = 0x128;
+
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// Sum over the aligned group of N consecutive lanes; every lane of the group
+// ends with the same bits (each step pairs lanes symmetrically).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group width");
+  if constexpr (N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRor8>(x);
+  return x;
+}
+
+// Reduce over lanes with equal (lane % N), N = lanes per token.
+template <int N>
+__device__ __forceinline__ float strided_sum(float x) {
+  if constexpr (N == 4) {
+    x += dpp<kDppRor4>(x);
+    x += dpp<kDppRor8>(x);
+  } else if constexpr (N == 8) {
+    x += dpp<kDppRor8>(x);
+  }
+  if constexpr (N <= 16) x += shfl_xor(x, 16);
+  x += shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float strided_max(float x) {
+  if constexpr (N == 4) {
+    x = fmaxf(x, dpp<kDppRor4>(x));
+    x = fmaxf(x, dpp<kDppRor8>(x));
+  } else if constexpr (N == 8) {
+    x = fmaxf(x, dpp<kDppRor8>(x));
+  }
+  if constexpr (N <= 16) x = fmaxf(x, shfl_xor(x, 16));
+  x = fmaxf(x, shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float uniform(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float h2f_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float h2f_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the .hip files).
+
+// Decode split pass: grid (n_runs * nspl, n_kv_heads, n_seqs), 64 threads.
+hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int g, hipStream_t st,
+                               bool* found);
+// Decode merge pass: grid (n_q_heads, n_seqs), 256 threads.
+hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
+// Prefill: workspace bytes a call needs (a multiple of 256, the last 256
+// bytes hold the checked-mode error word; 0 if none) and whether a kernel
+// exists for the tuple; then the launch.
+size_t prefill_workspace(const AttnArgs& a, int combo, int hd, int bs, int g, bool* found);
+hipError_t launch_prefill(const AttnArgs& a, int combo, int hd, int bs, int g, hipStream_t st,
+                          bool* found);
+// Resolver export.
+hipError_t launch_resolve(const AttnArgs& a, int bs, int n_cand, int32_t* rows_out, hipStream_t st);
+// Row copies for copy_cells.
+hipError_t launch_copy_rows(int phase, unsigned char* pool, unsigned char* stage,
+                            int64_t row_bytes, const int32_t* pairs, int32_t n_pairs,
+                            int64_t stage_offset_bytes, int64_t stage_row_stride, hipStream_t st);
+hipError_t launch_zero_words(int32_t* p, int n, hipStream_t st);
+
+}  // namespace pkv

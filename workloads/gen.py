@@ -438,3 +438,48 @@ def host_subset(w: Workload, seqs, k_pool, v_pool):
     kh = k_pool.index_select(0, idx).cpu().numpy()
     vh = v_pool.index_select(0, idx).cpu().numpy()
     return sub, kh, vh
+
+
+def make_custom(seed: int, n_seqs: int, n_q_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
+                fmts=("f16", "f16", "f16"), ctx=(1, 300), hole_frac: float = 0.05, mode: str = "causal",
+                n_runs: int = 4, kind: str = "decode", q_per_seq=(1, 40), pool_slack: int = 8,
+                max_blocks: Optional[int] = None) -> Workload:
+    """A random workload of any supported geometry: seq lengths ~ U{ctx},
+    blocks from one pool permutation, a fraction of non-final logical blocks
+    turned into holes, and random windows.  Spans are drawn to also reach
+    outside [0, seq_len); kv_map runs may overlap, be empty or stick out.
+    Prefill draws q_per_seq queries per sequence at sorted distinct
+    positions in [0, seq_len)."""
+    rng = np.random.default_rng(seed)
+    bs = block_size
+    L = rng.integers(ctx[0], ctx[1] + 1, size=n_seqs).astype(np.int32)
+    nblocks = [(int(c) + bs - 1) // bs for c in L]
+    mb = max_blocks or max(1, (ctx[1] + bs - 1) // bs)
+    pool = sum(nblocks) + pool_slack
+    table, _ = _tables_from_perm(rng.permutation(pool), nblocks, mb)
+    if hole_frac > 0:
+        _holes(rng, table, nblocks, hole_frac)
+    q_fmt, k_fmt, v_fmt = fmts
+    w = Workload(name="custom", cfg=0, seed=seed, n_seqs=n_seqs, n_q_heads=n_q_heads,
+                 n_kv_heads=n_kv_heads, head_dim=head_dim, block_size=bs, n_pool_blocks=pool,
+                 q_fmt=q_fmt, k_fmt=k_fmt, v_fmt=v_fmt, scale=1.0 / math.sqrt(head_dim),
+                 block_table=table, seq_lens=L, mode=mode, kind=kind)
+    win = np.zeros((n_seqs, 2), dtype=np.int32)
+    km = np.zeros((n_seqs, n_runs, 2), dtype=np.int32)
+    for s in range(n_seqs):
+        Ls = int(L[s])
+        a, b = sorted(rng.integers(-3, Ls + 4, size=2).tolist())
+        win[s] = (a, b)
+        for r in range(n_runs):
+            c = int(rng.integers(-2, Ls + 2))
+            n = int(rng.integers(-1, max(2, Ls // 3)))
+            km[s, r] = (c, n)
+    w.window = win
+    w.kv_map = km
+    if kind == "prefill":
+        nq = [int(rng.integers(q_per_seq[0], q_per_seq[1] + 1)) for _ in range(n_seqs)]
+        nq = [min(n, int(Ls)) for n, Ls in zip(nq, L)]
+        w.cu_q = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+        w.q_pos = np.concatenate([np.sort(rng.choice(int(Ls), size=n, replace=False))
+                                  for n, Ls in zip(nq, L)]).astype(np.int32)
+    return w
