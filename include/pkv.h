@@ -79,11 +79,12 @@ typedef enum {
 /*
  * Geometry of one attention call.
  *
- * Pools: k_pool and v_pool are [n_pool_blocks][block_size][row] where a row
- * is one token's entries for all kv heads: [n_kv_heads][head_dim] values for
- * f32/f16, or pkv_row_bytes(PKV_Q8_0, ...) bytes for q8_0 (per kv head,
- * head_dim/32 blocks of a little-endian f16 scale followed by 32 int8
- * codes; value = scale * code).  Pool row r = block * block_size + slot.
+ * Pools: k_pool and v_pool are [n_pool_blocks][n_kv_heads][block_size][seg]:
+ * inside a block, each kv head's block_size token entries are contiguous.
+ * seg is one token of one kv head: head_dim values for f32/f16, or for q8_0
+ * head_dim/32 blocks of a little-endian f16 scale followed by 32 int8 codes
+ * (value = scale * code), rounded up to whole 4-byte words.  Pool row
+ * (token cell) r = block * block_size + slot is that slot of every kv head.
  * block_table: int32 [n_seqs][max_blocks_per_seq].  seq_lens: int32
  * [n_seqs].  q head h reads kv head h / (n_q_heads / n_kv_heads).
  * Scores are scale * q.k.
@@ -112,9 +113,9 @@ typedef struct {
                            multiple of block_size, at most 64 blocks */
 } pkv_shape;
 
-/* Bytes of one pool row (one token, all kv heads) in format fmt; 0 when the
- * arguments are invalid.  A q8_0 row is rounded up to whole 4-byte words
- * ("KV Cache Design", section 3). */
+/* Bytes of one pool row (one token cell: all kv heads) in format fmt, i.e.
+ * n_kv_heads segments; 0 when the arguments are invalid.  A q8_0 segment is
+ * rounded up to whole 4-byte words ("KV Cache Design", section 3). */
 int64_t pkv_row_bytes(int32_t fmt, int32_t n_kv_heads, int32_t head_dim);
 
 /* ---------------------------------------------------------------------------
@@ -206,20 +207,24 @@ pkv_status pkv_paged_attn_prefill_window(const pkv_shape* shape, int32_t n_q_tot
  * count. */
 pkv_status pkv_order_moves(const int32_t* moves, int32_t n, int32_t* order_out, int32_t* n_out);
 
-/* Workspace for pkv_kv_copy_cells with these moves (an upper bound). */
+/* Workspace for pkv_kv_copy_cells with these moves (an upper bound);
+ * row_bytes_* = bytes of one token cell (all kv heads) of each pool. */
 size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t row_bytes_k,
                                       int64_t row_bytes_v);
 
-/* Apply moves (host int32 [n][3]) to k_pool and, if not NULL, v_pool
- * (device, n_pool_rows rows of row_bytes_k / row_bytes_v bytes; row bytes
- * a multiple of 4), bit-exact.  The host plans the moves (order_moves, then
- * the final source of every changed row), uploads the plan into the
- * workspace and waits for that upload, so `moves` may be freed on return;
- * the copies themselves run asynchronously on `stream`.  Every move must
- * lie inside [0, n_pool_rows) or the call is refused untouched. */
-pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int64_t n_pool_rows,
-                             int64_t row_bytes_k, int64_t row_bytes_v, const int32_t* moves,
-                             int32_t n, void* workspace, size_t workspace_bytes, void* stream);
+/* Apply moves (host int32 [n][3], in pool rows) to k_pool and, if not NULL,
+ * v_pool, bit-exact.  Both pools are [n_pool_blocks][n_kv_heads][block_size]
+ * [seg] (device; seg_bytes_k / seg_bytes_v bytes per token per kv head, a
+ * multiple of 4); a row is one slot of every kv head, so a move carries all
+ * kv heads of its tokens.  The host plans the moves (order_moves, then the
+ * final source of every changed row), uploads the plan into the workspace
+ * and waits for that upload, so `moves` may be freed on return; the copies
+ * run asynchronously on `stream`.  Every move must lie inside
+ * [0, n_pool_blocks * block_size) or the call is refused untouched. */
+pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, int32_t block_size,
+                             int32_t n_kv_heads, int64_t seg_bytes_k, int64_t seg_bytes_v,
+                             const int32_t* moves, int32_t n, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Debug export of the block-table/window resolver the attention kernels use.

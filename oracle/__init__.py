@@ -23,7 +23,7 @@ Arithmetic is float64 numpy; byte work is exact.  Readings of points the
 pages leave open are stated in the docstrings where they are used.
 """
 
-from .formats import row_bytes, decode_rows, f16_bits_to_f64  # noqa: F401
+from .formats import row_bytes, seg_bytes, decode_rows, f16_bits_to_f64  # noqa: F401
 from .attention import (  # noqa: F401
     INVALID_BLOCK,
     KV_MAP_MAX_SPANS,

@@ -8,10 +8,14 @@ row) is a whole number of Q8_0 blocks rounded up to whole f32 words.
 block_size tokens x n_kv_heads x head_dim, so one token's row holds every kv
 head.
 
-Reading: a row lists kv head 0's head_dim/32 blocks, then kv head 1's, ...;
-each block is the scale (2 bytes, little-endian IEEE half) followed by its
-32 signed codes; the dequantized value is scale * code, which is exact in
-float64 (and in float32).  The query is not quantized.
+Readings:
+* byte order inside a pool block: [kv head][slot][head_dim], i.e. a pool is
+  [n_blocks, n_kv_heads, block_size, W]; pool row r (token cell) is slot
+  r % block_size of block r // block_size, across all kv heads;
+* q8_0: one token of one kv head is head_dim/32 blocks, each the scale (2
+  bytes, little-endian IEEE half) followed by its 32 signed codes, rounded up
+  to whole 4-byte words; the dequantized value is scale * code, which is
+  exact in float64 (and in float32).  The query is not quantized.
 """
 
 from __future__ import annotations
@@ -22,19 +26,23 @@ Q8_BLOCK = 32
 Q8_BLOCK_BYTES = 2 + Q8_BLOCK
 
 
-def row_bytes(fmt: str, n_kv_heads: int, head_dim: int) -> int:
-    """Bytes of one pool row (one token, all kv heads)."""
+def seg_bytes(fmt: str, head_dim: int) -> int:
+    """Bytes of one token of one kv head."""
     if fmt == "f32":
-        return 4 * n_kv_heads * head_dim
+        return 4 * head_dim
     if fmt == "f16":
-        return 2 * n_kv_heads * head_dim
+        return 2 * head_dim
     if fmt == "q8_0":
         if head_dim % Q8_BLOCK:
             raise ValueError("q8_0 needs head_dim divisible by 32")
-        raw = n_kv_heads * (head_dim // Q8_BLOCK) * Q8_BLOCK_BYTES
-        words = -(-raw // 4)
-        return 4 * words
+        raw = (head_dim // Q8_BLOCK) * Q8_BLOCK_BYTES
+        return 4 * (-(-raw // 4))
     raise ValueError(f"unknown KV format {fmt!r}")
+
+
+def row_bytes(fmt: str, n_kv_heads: int, head_dim: int) -> int:
+    """Bytes of one token cell (all kv heads)."""
+    return n_kv_heads * seg_bytes(fmt, head_dim)
 
 
 def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -52,21 +60,18 @@ def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def decode_rows(pool: np.ndarray, fmt: str, rows: np.ndarray, n_kv_heads: int, head_dim: int) -> np.ndarray:
-    """Rows ``rows`` (flat pool row indices) of ``pool`` as float64
-    [len(rows), n_kv_heads, head_dim].
-
-    ``pool`` is either [n_blocks, bs, n_kv_heads, head_dim] (f32/f16) or uint8
-    [n_blocks, bs, row_bytes] (q8_0); it is viewed as flat rows."""
+    """Token cells ``rows`` (pool row r = block r // bs, slot r % bs) of
+    ``pool`` [n_blocks, n_kv_heads, bs, W] as float64 [len(rows), n_kv_heads,
+    head_dim]."""
     rows = np.asarray(rows, dtype=np.int64)
+    bs = pool.shape[2]
+    cells = pool[rows // bs, :, rows % bs]  # [n, n_kv_heads, W]
     if fmt in ("f32", "f16"):
-        flat = pool.reshape(-1, n_kv_heads, head_dim)
-        return flat[rows].astype(np.float64)
+        return cells.astype(np.float64)
     if fmt != "q8_0":
         raise ValueError(f"unknown KV format {fmt!r}")
-    rb = row_bytes("q8_0", n_kv_heads, head_dim)
-    flat = np.ascontiguousarray(pool).reshape(-1, rb)[rows]
     nb = head_dim // Q8_BLOCK
-    blocks = flat[:, : n_kv_heads * nb * Q8_BLOCK_BYTES].reshape(len(rows), n_kv_heads, nb, Q8_BLOCK_BYTES)
+    blocks = np.ascontiguousarray(cells[..., : nb * Q8_BLOCK_BYTES]).reshape(len(rows), n_kv_heads, nb, Q8_BLOCK_BYTES)
     bits = blocks[..., 0].astype(np.uint16) | (blocks[..., 1].astype(np.uint16) << 8)
     scale = f16_bits_to_f64(bits)
     codes = blocks[..., 2:].astype(np.uint8).view(np.int8).astype(np.float64)

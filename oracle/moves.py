@@ -17,7 +17,10 @@ Readings where the pages are silent:
   is defined as applying the moves one after another in that order, each as
   a memmove (the whole source run is read before it is written);
 * the same moves apply to the K pool and to the V pool; tables are not
-  touched.
+  touched;
+* a row is one token cell: in a pool laid out [n_blocks, n_kv_heads,
+  block_size, W], row r is slot r % block_size of block r // block_size
+  across every kv head (a plain 2-d array is a list of rows).
 """
 
 from __future__ import annotations
@@ -35,22 +38,32 @@ def order_moves(moves) -> list:
     return up + down
 
 
-def _rows(pool):
-    return pool.reshape(pool.shape[0] * pool.shape[1], -1) if pool.ndim > 2 else pool
+def _get(pool, idx):
+    if pool.ndim == 2:
+        return pool[idx].copy()
+    bs = pool.shape[2]
+    return pool[idx // bs, :, idx % bs].copy()
+
+
+def _set(pool, idx, val):
+    if pool.ndim == 2:
+        pool[idx] = val
+    else:
+        bs = pool.shape[2]
+        pool[idx // bs, :, idx % bs] = val
 
 
 def copy_cells(pools, moves):
     """Apply ``moves`` in order_moves order to every pool in ``pools`` (in
-    place).  A pool is a numpy array viewed as rows (first two axes of a
-    [blocks, bs, ...] pool flattened); each move copies its whole source run,
-    then writes it to the destination run (memmove)."""
+    place).  Each move copies its whole source run of rows, then writes it
+    to the destination run (memmove)."""
     mv = np.asarray(moves).reshape(-1, 3)
     order = order_moves(mv)
     for pool in pools:
-        rows = _rows(pool)
         for i in order:
             s, d, n = (int(x) for x in mv[i])
-            rows[d : d + n] = rows[s : s + n].copy()
+            src = np.arange(s, s + n)
+            _set(pool, np.arange(d, d + n), _get(pool, src))
     return pools
 
 
@@ -60,12 +73,11 @@ def copy_cells_rowwise(pools, moves):
     mv = np.asarray(moves).reshape(-1, 3)
     order = order_moves(mv)
     for pool in pools:
-        rows = _rows(pool)
         for i in order:
             s, d, n = (int(x) for x in mv[i])
             rng = range(n) if d < s else range(n - 1, -1, -1)
             for k in rng:
-                rows[d + k] = rows[s + k]
+                _set(pool, np.array([d + k]), _get(pool, np.array([s + k])))
     return pools
 
 

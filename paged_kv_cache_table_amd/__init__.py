@@ -5,8 +5,10 @@ include/pkv.h (pointers, sizes, the current HIP stream) and calls it; all
 computation runs in the library's HIP kernels.  If the library is missing,
 or a call is refused, the call raises: there is no fallback path.
 
-Formats follow the tensors' dtypes: float32 -> f32, float16 -> f16, and a
-uint8 K pool of shape [n_blocks, block_size, row_bytes] -> q8_0.
+Pools are [n_blocks, n_kv_heads, block_size, W] (inside a block, each kv
+head's token entries are contiguous).  Formats follow the tensors' dtypes:
+float32 -> f32, float16 -> f16, and a uint8 pool with W = q8_0 segment bytes
+-> q8_0.
 """
 
 from __future__ import annotations
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         "pkv_paged_attn_prefill_window": (I32, [SH, I32, I32, P, P, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
         "pkv_order_moves": (I32, [P, I32, P, P]),
         "pkv_copy_cells_workspace_bytes": (SZ, [P, I32, I64, I64]),
-        "pkv_kv_copy_cells": (I32, [P, P, I64, I64, I64, P, I32, P, SZ, P]),
+        "pkv_kv_copy_cells": (I32, [P, P, I32, I32, I32, I64, I64, P, I32, P, SZ, P]),
         "pkv_resolve_rows": (I32, [SH, I32, P, P, P, P, I32, I32, P, I32, P, P]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_char_p, []),
@@ -164,14 +166,16 @@ def row_bytes(fmt: int, n_kv_heads: int, head_dim: int) -> int:
 
 def make_shape(q, k_pool, v_pool, block_table, n_seqs: int, scale: float, flags: int = 0,
                split_tokens: int = 0) -> Shape:
-    """pkv_shape from the tensors: q [.., Hq, hd]; v_pool [NB, bs, Hkv, hd]."""
+    """pkv_shape from the tensors: q [.., Hq, hd]; v_pool [NB, Hkv, bs, hd]."""
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
         if not t.is_contiguous():
             raise TypeError(f"{name} must be contiguous")
     _i32(block_table, "block_table")
-    if v_pool.dim() != 4:
-        raise TypeError("v_pool must be [n_blocks, block_size, n_kv_heads, head_dim]")
-    nb, bs, hkv, hd = v_pool.shape
+    if v_pool.dim() != 4 or k_pool.dim() != 4:
+        raise TypeError("pools must be [n_blocks, n_kv_heads, block_size, W]")
+    nb, hkv, bs, hd = v_pool.shape
+    if tuple(k_pool.shape[:3]) != (nb, hkv, bs):
+        raise TypeError("k_pool and v_pool disagree on (n_blocks, n_kv_heads, block_size)")
     return Shape(n_seqs=n_seqs, n_q_heads=q.shape[-2], n_kv_heads=hkv, head_dim=hd, block_size=bs,
                  n_pool_blocks=nb, max_blocks_per_seq=block_table.shape[1], q_fmt=_fmt_of(q),
                  k_fmt=_fmt_of(k_pool), v_fmt=_fmt_of(v_pool), scale=scale, flags=flags,
@@ -213,7 +217,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, mo
                       split_tokens: int = 0, part: str = "both"):
     """Decode attention (one query per sequence) through the block table.
 
-    q [S, Hq, hd]; pools [NB, bs, Hkv, hd] (K may be uint8 q8_0 [NB, bs, row_bytes]);
+    q [S, Hq, hd]; pools [NB, Hkv, bs, hd] (K may be uint8 q8_0 [NB, Hkv, bs, seg]);
     block_table int32 [S, MB]; seq_lens int32 [S]; window int32 [S, 2] (span) or
     [S, n_runs, 2] (kv_map).  Returns (out float32 [S, Hq, hd], lse float32 [S, Hq]).
     part = "partials" / "merge" runs one of the two passes (same workspace)."""
@@ -316,24 +320,25 @@ def order_moves(moves) -> list:
 
 def kv_copy_cells(k_pool, v_pool, moves, workspace=None):
     """Apply (src, dst, len) row moves (host int32 array [n, 3]) to both pools
-    in order_moves order, bit-exact; pools are viewed as rows (first two axes)."""
+    in order_moves order, bit-exact.  Pools are [n_blocks, n_kv_heads,
+    block_size, W]; a row is one slot of every kv head."""
     import numpy as np
 
     torch = _torch()
     mv = np.ascontiguousarray(np.asarray(moves, dtype=np.int32).reshape(-1, 3))
     n = mv.shape[0]
-    n_rows = k_pool.shape[0] * k_pool.shape[1]
-    rbk = k_pool.numel() * k_pool.element_size() // n_rows
-    rbv = 0
-    if v_pool is not None:
-        if v_pool.shape[0] * v_pool.shape[1] != n_rows:
-            raise ValueError("K and V pools must have the same number of rows")
-        rbv = v_pool.numel() * v_pool.element_size() // n_rows
     for t in (k_pool, v_pool):
-        if t is not None and not t.is_contiguous():
-            raise TypeError("pools must be contiguous")
-    need = int(lib().pkv_copy_cells_workspace_bytes(mv.ctypes.data, n, rbk, max(rbv, 0)))
+        if t is not None and (not t.is_contiguous() or t.dim() != 4):
+            raise TypeError("pools must be contiguous [n_blocks, n_kv_heads, block_size, W]")
+    nb, hkv, bs = k_pool.shape[:3]
+    seg_k = k_pool.shape[3] * k_pool.element_size()
+    seg_v = 0
+    if v_pool is not None:
+        if tuple(v_pool.shape[:3]) != (nb, hkv, bs):
+            raise ValueError("K and V pools must agree on (n_blocks, n_kv_heads, block_size)")
+        seg_v = v_pool.shape[3] * v_pool.element_size()
+    need = int(lib().pkv_copy_cells_workspace_bytes(mv.ctypes.data, n, seg_k * hkv, seg_v * hkv))
     ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=k_pool.device)
-    _check(lib().pkv_kv_copy_cells(_ptr(k_pool), _ptr(v_pool), n_rows, rbk, rbv, mv.ctypes.data, n,
+    _check(lib().pkv_kv_copy_cells(_ptr(k_pool), _ptr(v_pool), nb, bs, hkv, seg_k, seg_v, mv.ctypes.data, n,
                                    _ptr(ws), ws.numel(), _stream(k_pool)))
     return k_pool, v_pool

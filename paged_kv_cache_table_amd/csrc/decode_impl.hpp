@@ -38,6 +38,7 @@ template <int HD, int G>
 struct KPathF16 {
   static constexpr int LPT = HD / 16;
   static constexpr int KW = 8;
+  static constexpr int kQRegs = G * 8;
   static constexpr int64_t kHeadBytes = HD * 2;
   uint32_t q[G][8];
 
@@ -75,6 +76,7 @@ template <int HD, int G>
 struct KPathF32 {
   static constexpr int LPT = HD / 16;
   static constexpr int KW = 16;
+  static constexpr int kQRegs = G * 16;
   static constexpr int64_t kHeadBytes = HD * 4;
   float q[G][16];
 
@@ -118,6 +120,7 @@ template <int HD, int G, bool QF32>
 struct KPathQ8 {
   static constexpr int LPT = HD / 16;
   static constexpr int KW = 6;  // 5 dwords around the codes, 1 with the scale
+  static constexpr int kQRegs = G * 16;
   static constexpr int64_t kHeadBytes = HD / 32 * 34;
   float q[G][16];
   int code_off, code_shift, scale_off;
@@ -184,16 +187,13 @@ struct VPathF16 {
     w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
   }
-  __device__ __forceinline__ static void to_float(const uint32_t (&w)[VW], float (&f)[16]) {
+  // acc += p * v with the f16 -> f32 conversion folded into the FMA
+  __device__ __forceinline__ static void fma_acc(const uint32_t (&w)[VW], float p, float (&acc)[16]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      f[2 * i] = h2f_lo(w[i]);
-      f[2 * i + 1] = h2f_hi(w[i]);
+      acc[2 * i] = fmaf(p, h2f_lo(w[i]), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(p, h2f_hi(w[i]), acc[2 * i + 1]);
     }
-  }
-  // element e of lane sub is head dimension d
-  __device__ __forceinline__ static int dim(int sub, int e) {
-    return e < 8 ? 8 * sub + e : 8 * (sub + LPT) + (e - 8);
   }
   static constexpr int kChunks = 2;  // contiguous runs of 8 floats
   __device__ __forceinline__ static int chunk_dim(int sub, int c) { return 8 * (sub + LPT * c); }
@@ -213,9 +213,9 @@ struct VPathF32 {
       w[4 * c + 0] = x.x; w[4 * c + 1] = x.y; w[4 * c + 2] = x.z; w[4 * c + 3] = x.w;
     }
   }
-  __device__ __forceinline__ static void to_float(const uint32_t (&w)[VW], float (&f)[16]) {
+  __device__ __forceinline__ static void fma_acc(const uint32_t (&w)[VW], float p, float (&acc)[16]) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) f[i] = __builtin_bit_cast(float, w[i]);
+    for (int i = 0; i < 16; ++i) acc[i] = fmaf(p, __builtin_bit_cast(float, w[i]), acc[i]);
   }
   static constexpr int kChunks = 4;
   __device__ __forceinline__ static int chunk_dim(int sub, int c) { return 4 * (sub + LPT * c); }
@@ -250,12 +250,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
   constexpr int LPT = HD / 16;   // lanes per token row
   constexpr int TPP = 64 / LPT;  // tokens per pass
   static_assert(BS % TPP == 0, "block size must be a multiple of tokens per pass");
-  constexpr int NP = BS / TPP;            // passes per block
-  constexpr int NPU = NP < 2 ? NP : 2;    // passes per pipelined unit
-  constexpr int NU = NP / NPU;            // units per block
+  constexpr int NU = BS / TPP;  // passes per block; a pass is the pipelined unit
   constexpr int KW = KP::KW, VW = VP::VW;
+  // Register ring of one-pass units: as many as fit next to q, the running
+  // outputs and the temporaries in 256 VGPRs (2 waves per SIMD); the loads
+  // run RING-1 units ahead of compute.
+  constexpr int kBudget = 232 - KP::kQRegs - 16 * G - 24;
+  constexpr int kRingFit = kBudget / (KW + VW);
+  constexpr int RING = kRingFit < 2 ? 2 : (kRingFit > 8 ? 8 : kRingFit);
+  constexpr float kEmpty = -1e30f;  // running max before any visible token
 
-  const int slot = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  // kv head is the fastest grid index: the Hkv waves that read interleaved
+  // slices of the same pool rows are dispatched together.
+  const int kvh = blockIdx.x, slot = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x, tok = lane / LPT, sub = lane % LPT;
   const int32_t L = clamp_seq_len(a.seq_lens[s], a.max_blocks, BS);
   int32_t lo, hi;
@@ -266,113 +273,132 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
   const int32_t nblk = (hi - 1) / BS - jb0 + 1;  // <= 64 by construction
   int32_t myid = -1;
   if (lane < nblk) myid = block_id(a, s, jb0 + lane, kvh == 0);
-  const uint64_t mask = __ballot(myid >= 0);
+  // The ballot is wave-uniform; readfirstlane makes that visible to the
+  // compiler, so loops over it stay scalar (no exec-masked flow blocks).
+  const uint64_t bal = __ballot(myid >= 0);
+  const uint64_t mask = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(bal >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bal);
 
   KP kp;
   const int64_t qoff = ((int64_t)s * a.n_q_heads + (int64_t)kvh * G) * HD;
   kp.load_q((const QT*)a.q + qoff, sub);
 
+  // m: running max of the scaled scores (log2 domain), wave-uniform; l and
+  // acc: this lane's running sum and output for its tokens, all relative to m.
   float m[G], l[G], acc[G][16];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
+    m[h] = kEmpty;
     l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
   }
 
-  const unsigned char* kbase = a.k_pool + (int64_t)kvh * KP::kHeadBytes;
-  const unsigned char* vbase = a.v_pool + (int64_t)kvh * VP::kHeadBytes;
-  const int64_t krb = a.k_row_bytes, vrb = a.v_row_bytes;
+  // Pool layout [block][kv head][slot][head]: this wave's (block, kv head)
+  // tile is block_size contiguous token entries.
+  const unsigned char* kbase = a.k_pool + (int64_t)kvh * BS * KP::kHeadBytes;
+  const unsigned char* vbase = a.v_pool + (int64_t)kvh * BS * VP::kHeadBytes;
+  const int64_t kbb = a.k_block_bytes, vbb = a.v_block_bytes;
 
   struct Unit {
-    uint32_t k[NPU][KW];
-    uint32_t v[NPU][VW];
+    uint32_t k[KW];
+    uint32_t v[VW];
   };
   auto load_unit = [&](Unit& U, int j, int u) {
     const int32_t blk = __builtin_amdgcn_readlane(myid, j);
-    const int64_t row0 = (int64_t)blk * BS + u * (NPU * TPP) + tok;
-#pragma unroll
-    for (int p = 0; p < NPU; ++p) {
-      const int64_t row = row0 + p * TPP;
-      kp.load_k(kbase + row * krb, sub, U.k[p]);
-      VP::load(vbase + row * vrb, sub, U.v[p]);
-    }
+    const int slot = u * TPP + tok;
+    kp.load_k(kbase + blk * kbb + slot * KP::kHeadBytes, sub, U.k);
+    VP::load(vbase + blk * vbb + slot * VP::kHeadBytes, sub, U.v);
   };
-  auto compute = [&](const Unit& U, int j, int u) {
-    const int32_t pos0 = (jb0 + j) * BS + u * (NPU * TPP);
-    const bool full = pos0 >= lo && pos0 + NPU * TPP <= hi;
-    float sc[NPU][G];
+  auto compute = [&](Unit& U, int j, int u) {
+    const int32_t pos0 = (jb0 + j) * BS + u * TPP;
+    const bool full = pos0 >= lo && pos0 + TPP <= hi;  // wave-uniform
+    float sc[G];
+    kp.dot(U.k, sc);
 #pragma unroll
-    for (int p = 0; p < NPU; ++p) {
-      kp.dot(U.k[p], sc[p]);
-      const int32_t t = pos0 + p * TPP + tok;
-      const bool ok = full || (t >= lo && t < hi);
+    for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT>(sc[h]) * a.score_mul;
+    if (!full) {
+      // window edge: positions outside [lo, hi) get score -inf and value 0
+      // (selected, never multiplied, so NaN in those rows cannot leak in)
+      const int32_t t = pos0 + tok;
+      const bool ok = t >= lo && t < hi;
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = ok ? sc[h] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < VW; ++i) U.v[i] = ok ? U.v[i] : 0u;
+    }
+    // The max only moves when some score exceeds it; most units skip the
+    // cross-lane reduction and the rescale entirely.
+    bool above = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) above |= sc[h] > m[h];
+    if (__builtin_amdgcn_ballot_w64(above)) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float x = group_sum<LPT>(sc[p][h]) * a.score_mul;
-        sc[p][h] = ok ? x : -INFINITY;
+        const float mn = fmaxf(m[h], wave_max_tokens<LPT>(sc[h]));
+        const float alpha = fast_exp2(m[h] - mn);  // 1 if unchanged, 0 from empty
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
+        m[h] = mn;
       }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float bm = sc[0][h];
-#pragma unroll
-      for (int p = 1; p < NPU; ++p) bm = fmaxf(bm, sc[p][h]);
-      bm = uniform(strided_max<LPT>(bm));
-      if (bm > m[h]) {
-        const float alpha = fast_exp2(m[h] - bm);
-        l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
-        m[h] = bm;
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < NPU; ++p) {
-      float vf[16];
-      VP::to_float(U.v[p], vf);
-      if (!full) {
-        const int32_t t = pos0 + p * TPP + tok;
-        const bool ok = t >= lo && t < hi;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) vf[e] = ok ? vf[e] : 0.f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pr = m[h] == -INFINITY ? 0.f : fast_exp2(sc[p][h] - m[h]);
-        l[h] += pr;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
-      }
+      const float pr = fast_exp2(sc[h] - m[h]);  // -inf -> 0
+      l[h] += pr;
+      VP::fma_acc(U.v, pr, acc[h]);
     }
   };
 
-  if (mask) {
-    int cj = __builtin_ctzll(mask), cu = 0;
-    Unit cur;
-    load_unit(cur, cj, cu);
-    while (true) {
-      int nj = cj, nu = cu + 1;
-      bool has_next = true;
-      if (nu == NU) {
-        const uint64_t rest = cj >= 63 ? 0ull : (mask & (~0ull << (cj + 1)));
-        if (rest) {
-          nj = __builtin_ctzll(rest);
-          nu = 0;
-        } else {
-          has_next = false;
-        }
+  // Units (one pass each) run in order over the non-hole blocks; loads run
+  // RING-1 units ahead of compute through a ring of RING register buffers.
+  // The ring is unrolled so every buffer keeps a fixed role.  The body has a
+  // fixed number of steps with one exit at its top: an exit in the middle
+  // would become an exec-masked flow block whose join makes the compiler
+  // drain all outstanding loads.  Steps past the last unit load that unit
+  // again (cache hits) and skip the compute, so the number of loads issued
+  // after any unit is fixed and each wait leaves the later loads in flight.
+  struct Cursor {
+    uint64_t rest;  // blocks after j still to visit
+    int j, u;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.u == NU) {
+      c.u = 0;
+      c.j = c.rest ? __builtin_ctzll(c.rest) : 64;
+      c.rest &= c.rest - 1;
+    }
+  };
+  const int n_units = __builtin_popcountll(mask) * NU;
+  if (n_units > 0) {
+    Cursor lc;
+    lc.j = __builtin_ctzll(mask);
+    lc.rest = mask & (mask - 1);
+    lc.u = 0;
+    Cursor cc = lc;
+    int issued = 0;
+    auto load_next = [&](Unit& U) {
+      load_unit(U, lc.j, lc.u);
+      if (++issued < n_units) advance(lc);
+    };
+    const int n_pad = (n_units + RING - 1) / RING * RING;
+    Unit buf[RING];
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r) load_next(buf[r]);
+    for (int i = 0; i < n_pad; i += RING) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        load_next(buf[(r + RING - 1) % RING]);
+        if (cc.j < 64) compute(buf[r], cc.j, cc.u);
+        advance(cc);
       }
-      Unit nxt;
-      if (has_next) load_unit(nxt, nj, nu);
-      compute(cur, cj, cu);
-      if (!has_next) break;
-      cur = nxt;
-      cj = nj;
-      cu = nu;
     }
   }
+  // A wave that saw no visible token reports an empty partial.
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (m[h] == kEmpty) m[h] = -INFINITY;
 
   // Sum lanes that hold the same elements (all share the wave-wide max).
 #pragma unroll
@@ -409,62 +435,64 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
 
 // Merge the split slots of one (sequence, q head) by log-sum-exp:
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, lse = (M + log2 L) ln 2.
+// One workgroup per (64-wide slice of head_dim, q head, sequence); its four
+// waves take every fourth slot (lane = dimension), so four slot rows are in
+// flight per step, and combine through LDS in a fixed order.
 template <int HD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
-  constexpr int NG = 256 / HD;  // slot groups
-  const int h = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
+  const int dc = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int nslot = a.n_runs * a.nspl;
+  const int32_t lim = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
+  const int64_t row0 = (int64_t)s * nslot * a.n_q_heads + h;  // slot stride n_q_heads
   __shared__ float red[256];
   __shared__ float red2[256];
-  const int32_t lim = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
 
   float M = -INFINITY;
   for (int slot = t; slot < nslot; slot += 256) {
     int32_t lo, hi;
     split_range(a, s, slot, lim, lo, hi);
-    if (lo < hi) M = fmaxf(M, a.part_ml[(((int64_t)s * nslot + slot) * a.n_q_heads + h) * 2]);
+    if (lo < hi) M = fmaxf(M, a.part_ml[(row0 + (int64_t)slot * a.n_q_heads) * 2]);
   }
   red[t] = M;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+  for (int k = 128; k > 0; k >>= 1) {
+    if (t < k) red[t] = fmaxf(red[t], red[t + k]);
     __syncthreads();
   }
   M = red[0];
   __syncthreads();
 
-  const int d = t % HD, grp = t / HD;
+  const int d = dc * 64 + lane;
   float acc = 0.f, lsum = 0.f;
   if (M != -INFINITY) {
-    for (int slot = grp; slot < nslot; slot += NG) {
+#pragma unroll 4
+    for (int slot = w; slot < nslot; slot += 4) {
       int32_t lo, hi;
       split_range(a, s, slot, lim, lo, hi);
       if (lo >= hi) continue;
-      const int64_t base = ((int64_t)s * nslot + slot) * a.n_q_heads + h;
-      const float mi = a.part_ml[base * 2];
-      if (mi == -INFINITY) continue;
-      const float w = fast_exp2(mi - M);
-      acc = fmaf(w, a.part_o[base * HD + d], acc);
-      lsum = fmaf(w, a.part_ml[base * 2 + 1], lsum);
+      const int64_t r = row0 + (int64_t)slot * a.n_q_heads;
+      const float2 ml = *(const float2*)(a.part_ml + r * 2);
+      if (ml.x == -INFINITY) continue;
+      const float wgt = fast_exp2(ml.x - M);
+      acc = fmaf(wgt, a.part_o[r * HD + d], acc);
+      lsum = fmaf(wgt, ml.y, lsum);
     }
   }
   red[t] = acc;
   red2[t] = lsum;
   __syncthreads();
-  if (grp == 0) {
-    float sa = red[d], sl = red2[d];
-#pragma unroll
-    for (int g2 = 1; g2 < NG; ++g2) {
-      sa += red[g2 * HD + d];
-      sl += red2[g2 * HD + d];
-    }
+  if (w == 0) {
+    const float sa = (red[lane] + red[64 + lane]) + (red[128 + lane] + red[192 + lane]);
+    const float sl = (red2[lane] + red2[64 + lane]) + (red2[128 + lane] + red2[192 + lane]);
     const int64_t o = ((int64_t)s * a.n_q_heads + h) * HD + d;
     if (M == -INFINITY) {
       a.out[o] = 0.f;
-      if (a.lse && d == 0) a.lse[(int64_t)s * a.n_q_heads + h] = -INFINITY;
+      if (a.lse && dc == 0 && lane == 0) a.lse[(int64_t)s * a.n_q_heads + h] = -INFINITY;
     } else {
       a.out[o] = sa / sl;
-      if (a.lse && d == 0) a.lse[(int64_t)s * a.n_q_heads + h] = (M + __builtin_amdgcn_logf(sl)) * kLn2;
+      if (a.lse && dc == 0 && lane == 0)
+        a.lse[(int64_t)s * a.n_q_heads + h] = (M + __builtin_amdgcn_logf(sl)) * kLn2;
     }
   }
 }

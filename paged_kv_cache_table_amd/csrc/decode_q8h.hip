@@ -5,7 +5,7 @@ namespace pkv {
 
 hipError_t launch_decode_split_q8h(const AttnArgs& a, int hd, int bs, int g, hipStream_t st,
                                      bool* found) {
-  const dim3 grid(a.n_runs * a.nspl, a.n_kv_heads, a.n_seqs);
+  const dim3 grid(a.n_kv_heads, a.n_runs * a.nspl, a.n_seqs);
 #define PKV_CASE(HD, BS, G)                                                                \
   if (hd == HD && bs == BS && g == G) {                                                    \
     hipLaunchKernelGGL((decode_split_kernel<HD, BS, G, kComboQ8H>), grid, dim3(64), 0, st, a); \

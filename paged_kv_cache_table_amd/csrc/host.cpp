@@ -42,18 +42,25 @@ const char* fmt_name(int f) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int64_t row_bytes_of(int fmt, int hkv, int hd) {
-  if (hkv <= 0 || hd <= 0) return 0;
+// Bytes of one token of one kv head: head_dim values, or for q8_0 head_dim/32
+// blocks of (f16 scale, 32 int8) rounded up to whole 4-byte words.
+int64_t seg_bytes_of(int fmt, int hd) {
+  if (hd <= 0) return 0;
   switch (fmt) {
-    case PKV_F32: return 4ll * hkv * hd;
-    case PKV_F16: return 2ll * hkv * hd;
+    case PKV_F32: return 4ll * hd;
+    case PKV_F16: return 2ll * hd;
     case PKV_Q8_0: {
       if (hd % 32) return 0;
-      const int64_t raw = (int64_t)hkv * (hd / 32) * 34;
+      const int64_t raw = (int64_t)(hd / 32) * 34;
       return (raw + 3) / 4 * 4;
     }
     default: return 0;
   }
+}
+
+int64_t row_bytes_of(int fmt, int hkv, int hd) {
+  if (hkv <= 0) return 0;
+  return (int64_t)hkv * seg_bytes_of(fmt, hd);
 }
 
 bool supported_head_block(int hd, int bs) {
@@ -154,7 +161,11 @@ pkv_status plan_decode(const pkv_shape* sh, int mode, int n_runs, const void* wi
   }
   const int64_t ctx = (int64_t)sh->max_blocks_per_seq * sh->block_size;
   const int64_t nspl = (ctx + split - 1) / split;
-  if (nspl * P->runs > INT32_MAX / 2) return fail(PKV_E_ARG, "too many split slots");
+  if (nspl * P->runs > 65535)
+    return fail(PKV_E_UNSUPPORTED,
+                "%lld split slots per sequence (max_blocks_per_seq %d x block %d / split %d x %d runs) "
+                "exceed 65535; use a larger split_tokens",
+                (long long)(nspl * P->runs), sh->max_blocks_per_seq, sh->block_size, split, P->runs);
   P->split = split;
   P->nspl = (int)nspl;
   const size_t slots = (size_t)sh->n_seqs * nspl * P->runs * sh->n_q_heads;
@@ -173,8 +184,10 @@ pkv::AttnArgs base_args(const pkv_shape* sh, const Plan& P) {
   a.n_pool_blocks = sh->n_pool_blocks;
   a.max_blocks = sh->max_blocks_per_seq;
   a.block_size = sh->block_size;
-  a.k_row_bytes = row_bytes_of(sh->k_fmt, sh->n_kv_heads, sh->head_dim);
-  a.v_row_bytes = row_bytes_of(sh->v_fmt, sh->n_kv_heads, sh->head_dim);
+  a.k_seg_bytes = seg_bytes_of(sh->k_fmt, sh->head_dim);
+  a.v_seg_bytes = seg_bytes_of(sh->v_fmt, sh->head_dim);
+  a.k_block_bytes = a.k_seg_bytes * sh->n_kv_heads * sh->block_size;
+  a.v_block_bytes = a.v_seg_bytes * sh->n_kv_heads * sh->block_size;
   a.score_mul = (float)((double)sh->scale * 1.4426950408889634);
   a.flags = sh->flags;
   a.n_runs = P.runs;
@@ -418,18 +431,23 @@ size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t r
          align_up((size_t)rows * (size_t)row_bytes_v, 256) + 256;
 }
 
-pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int64_t n_pool_rows, int64_t row_bytes_k,
-                             int64_t row_bytes_v, const int32_t* moves, int32_t n, void* ws,
-                             size_t ws_bytes, void* stream) {
+pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, int32_t block_size,
+                             int32_t n_kv_heads, int64_t seg_bytes_k, int64_t seg_bytes_v,
+                             const int32_t* moves, int32_t n, void* ws, size_t ws_bytes,
+                             void* stream) {
   if (!k_pool) return fail(PKV_E_ARG, "k_pool is NULL");
   if (n < 0) return fail(PKV_E_ARG, "negative move count %d", n);
   if (n > 0 && !moves) return fail(PKV_E_ARG, "moves is NULL");
-  if (n_pool_rows <= 0 || n_pool_rows > INT32_MAX)
-    return fail(PKV_E_ARG, "n_pool_rows %lld outside [1, 2^31)", (long long)n_pool_rows);
-  if (row_bytes_k <= 0 || row_bytes_k % 4)
-    return fail(PKV_E_ARG, "row_bytes_k %lld must be a positive multiple of 4", (long long)row_bytes_k);
-  if (v_pool && (row_bytes_v <= 0 || row_bytes_v % 4))
-    return fail(PKV_E_ARG, "row_bytes_v %lld must be a positive multiple of 4", (long long)row_bytes_v);
+  if (n_pool_blocks <= 0 || block_size <= 0 || n_kv_heads <= 0)
+    return fail(PKV_E_ARG, "n_pool_blocks %d, block_size %d and n_kv_heads %d must be positive",
+                n_pool_blocks, block_size, n_kv_heads);
+  const int64_t n_pool_rows = (int64_t)n_pool_blocks * block_size;
+  if (n_pool_rows > INT32_MAX)
+    return fail(PKV_E_ARG, "%lld pool rows exceed 2^31 - 1", (long long)n_pool_rows);
+  if (seg_bytes_k <= 0 || seg_bytes_k % 4)
+    return fail(PKV_E_ARG, "seg_bytes_k %lld must be a positive multiple of 4", (long long)seg_bytes_k);
+  if (v_pool && (seg_bytes_v <= 0 || seg_bytes_v % 4))
+    return fail(PKV_E_ARG, "seg_bytes_v %lld must be a positive multiple of 4", (long long)seg_bytes_v);
   int64_t lo = INT64_MAX, hi = -1;
   for (int32_t i = 0; i < n; ++i) {
     const int64_t s = moves[3 * i], d = moves[3 * i + 1], len = moves[3 * i + 2];
@@ -477,35 +495,37 @@ pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int64_t n_pool_rows, in
     scatter.push_back((int32_t)r);
     scatter.push_back(y);
   }
+  const int64_t row_k = seg_bytes_k * n_kv_heads, row_v = v_pool ? seg_bytes_v * n_kv_heads : 0;
   const size_t idx_bytes = align_up((gather.size() + scatter.size()) * sizeof(int32_t), 256);
-  const size_t stage_k = align_up((size_t)n_stage * (size_t)row_bytes_k, 256);
-  const size_t stage_v = v_pool ? align_up((size_t)n_stage * (size_t)row_bytes_v, 256) : 0;
+  const size_t stage_k = align_up((size_t)n_stage * (size_t)row_k, 256);
+  const size_t stage_v = align_up((size_t)n_stage * (size_t)row_v, 256);
   const size_t need = idx_bytes + stage_k + stage_v;
   if (!ws || ws_bytes < need)
     return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 ws ? ws_bytes : (size_t)0, need);
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t st = (hipStream_t)stream;
   std::vector<int32_t> idx(gather);
   idx.insert(idx.end(), scatter.begin(), scatter.end());
   int32_t* d_idx = (int32_t*)ws;
   unsigned char* stage = (unsigned char*)ws + idx_bytes;
   hipError_t e = hipMemcpyAsync(d_idx, idx.data(), idx.size() * sizeof(int32_t),
-                                hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
+                                hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return device_fail(e, "uploading the move plan");
   const int32_t n_gather = (int32_t)(gather.size() / 2), n_scatter = (int32_t)(scatter.size() / 2);
   const int32_t* d_gather = d_idx;
   const int32_t* d_scatter = d_idx + gather.size();
-  struct Pool { unsigned char* p; int64_t rb; size_t off; } pools[2] = {
-      {(unsigned char*)k_pool, row_bytes_k, 0}, {(unsigned char*)v_pool, row_bytes_v, stage_k}};
+  struct Pool { pkv::PoolGeom g; unsigned char* stage; } pools[2] = {
+      {{(unsigned char*)k_pool, seg_bytes_k, n_kv_heads, block_size}, stage},
+      {{(unsigned char*)v_pool, seg_bytes_v, n_kv_heads, block_size}, stage + stage_k}};
   for (const Pool& pl : pools) {
-    if (!pl.p) continue;
-    e = pkv::launch_copy_rows(1, pl.p, stage, pl.rb, d_gather, n_gather, (int64_t)pl.off, pl.rb, s);
+    if (!pl.g.base) continue;
+    e = pkv::launch_copy_rows(1, pl.g, pl.stage, d_gather, n_gather, st);
     if (e != hipSuccess) return device_fail(e, "copy_cells gather launch");
   }
   for (const Pool& pl : pools) {
-    if (!pl.p) continue;
-    e = pkv::launch_copy_rows(2, pl.p, stage, pl.rb, d_scatter, n_scatter, (int64_t)pl.off, pl.rb, s);
+    if (!pl.g.base) continue;
+    e = pkv::launch_copy_rows(2, pl.g, pl.stage, d_scatter, n_scatter, st);
     if (e != hipSuccess) return device_fail(e, "copy_cells scatter launch");
   }
   return ok();

@@ -34,7 +34,9 @@ struct AttnArgs {
   int32_t mode, n_runs;  // n_runs = runs per sequence (1 unless kv_map)
   int32_t split, nspl;   // decode: tokens per split, split slots per run
   int32_t n_q_total, max_q;
-  int64_t k_row_bytes, v_row_bytes;
+  // Pool layout [n_blocks][n_kv_heads][block_size][seg]: seg = bytes of one
+  // token of one kv head; a block is n_kv_heads * block_size * seg bytes.
+  int64_t k_seg_bytes, v_seg_bytes, k_block_bytes, v_block_bytes;
   float score_mul;  // scale * log2(e): scores are kept in the log2 domain
   uint32_t flags;
 };
@@ -148,17 +150,23 @@ __device__ __forceinline__ float strided_sum(float x) {
   return x;
 }
 
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Max over the wave of a value that is equal on the N lanes of each token
+// group (N = lanes per token).  Within a 16-lane row the token groups are
+// combined with DPP rotations; the four rows are then read into scalar
+// registers, so the result is wave-uniform and no LDS round trip is needed.
 template <int N>
-__device__ __forceinline__ float strided_max(float x) {
+__device__ __forceinline__ float wave_max_tokens(float x) {
   if constexpr (N == 4) {
     x = fmaxf(x, dpp<kDppRor4>(x));
     x = fmaxf(x, dpp<kDppRor8>(x));
   } else if constexpr (N == 8) {
     x = fmaxf(x, dpp<kDppRor8>(x));
   }
-  if constexpr (N <= 16) x = fmaxf(x, shfl_xor(x, 16));
-  x = fmaxf(x, shfl_xor(x, 32));
-  return x;
+  return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 
 __device__ __forceinline__ float uniform(float x) {
@@ -177,10 +185,10 @@ __device__ __forceinline__ float h2f_hi(uint32_t w) {
 // ---------------------------------------------------------------------------
 // Launchers (defined in the .hip files).
 
-// Decode split pass: grid (n_runs * nspl, n_kv_heads, n_seqs), 64 threads.
+// Decode split pass: grid (n_kv_heads, n_runs * nspl, n_seqs), 64 threads.
 hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int g, hipStream_t st,
                                bool* found);
-// Decode merge pass: grid (n_q_heads, n_seqs), 256 threads.
+// Decode merge pass: grid (head_dim / 64, n_q_heads, n_seqs), 256 threads.
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
 // Prefill: workspace bytes a call needs (a multiple of 256, the last 256
 // bytes hold the checked-mode error word; 0 if none) and whether a kernel
@@ -190,10 +198,14 @@ hipError_t launch_prefill(const AttnArgs& a, int combo, int hd, int bs, int g, h
                           bool* found);
 // Resolver export.
 hipError_t launch_resolve(const AttnArgs& a, int bs, int n_cand, int32_t* rows_out, hipStream_t st);
-// Row copies for copy_cells.
-hipError_t launch_copy_rows(int phase, unsigned char* pool, unsigned char* stage,
-                            int64_t row_bytes, const int32_t* pairs, int32_t n_pairs,
-                            int64_t stage_offset_bytes, int64_t stage_row_stride, hipStream_t st);
+// Row copies for copy_cells: a row (token cell) is n_kv_heads segments of
+// seg_bytes, one per kv head, block_size * seg_bytes apart.
+struct PoolGeom {
+  unsigned char* base;
+  int64_t seg_bytes, n_kv_heads, block_size;
+};
+hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stage,
+                            const int32_t* pairs, int32_t n_pairs, hipStream_t st);
 hipError_t launch_zero_words(int32_t* p, int n, hipStream_t st);
 
 }  // namespace pkv

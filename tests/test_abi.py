@@ -46,6 +46,7 @@ def test_row_bytes_golden():
     with open(os.path.join(GOLDEN, "q8_0_row_bytes.json")) as f:
         for c in json.load(f)["cases"]:
             assert pkv.row_bytes(pkv.Q8_0, c["n_kv_heads"], c["head_dim"]) == c["row_bytes"]
+            assert pkv.row_bytes(pkv.Q8_0, 1, c["head_dim"]) == c["segment_bytes"]
     assert pkv.row_bytes(pkv.F16, 8, 128) == 2048
     assert pkv.row_bytes(pkv.F32, 2, 64) == 512
     assert pkv.row_bytes(pkv.Q8_0, 1, 48) == 0
@@ -135,13 +136,16 @@ def test_decode_workspace_size_formula():
 def test_copy_cells_refuses_out_of_range_moves():
     L = pkv.lib()
     mv = np.array([[0, 5, 3], [10, 98, 4]], dtype=np.int32)
-    st = L.pkv_kv_copy_cells(FAKE, FAKE, 100, 64, 64, mv.ctypes.data, 2, FAKE, 1 << 30, None)
+    # 25 blocks x 4 slots = 100 rows, 2 kv heads of 32-byte segments
+    st = L.pkv_kv_copy_cells(FAKE, FAKE, 25, 4, 2, 32, 32, mv.ctypes.data, 2, FAKE, 1 << 30, None)
     assert st == 1 and "move 1" in pkv.last_error()
-    st = L.pkv_kv_copy_cells(FAKE, FAKE, 100, 62, 64, mv.ctypes.data, 1, FAKE, 1 << 30, None)
-    assert st == 1 and "row_bytes_k" in pkv.last_error()
+    st = L.pkv_kv_copy_cells(FAKE, FAKE, 25, 4, 2, 30, 32, mv.ctypes.data, 1, FAKE, 1 << 30, None)
+    assert st == 1 and "seg_bytes_k" in pkv.last_error()
+    st = L.pkv_kv_copy_cells(FAKE, FAKE, 25, 0, 2, 32, 32, mv.ctypes.data, 1, FAKE, 1 << 30, None)
+    assert st == 1 and "block_size" in pkv.last_error()
     # no effective move: nothing to do, nothing touched
     mv0 = np.array([[3, 3, 5], [1, 9, 0]], dtype=np.int32)
-    assert L.pkv_kv_copy_cells(FAKE, FAKE, 100, 64, 64, mv0.ctypes.data, 2, None, 0, None) == 0
+    assert L.pkv_kv_copy_cells(FAKE, FAKE, 25, 4, 2, 32, 32, mv0.ctypes.data, 2, None, 0, None) == 0
 
 
 def test_copy_cells_workspace_bound():

@@ -127,9 +127,8 @@ def test_one_hot_row_ids():
     w.window = np.stack([t, t + 1], 1).astype(np.int32)
     d = Dev(w)
     n_rows = w.n_pool_blocks * w.block_size
-    rowid = torch.arange(n_rows, dtype=torch.float32, device="cuda")
-    v = rowid[:, None, None].expand(n_rows, w.n_kv_heads, w.head_dim).contiguous()
-    v = v.reshape(w.n_pool_blocks, w.block_size, w.n_kv_heads, w.head_dim)
+    rowid = torch.arange(n_rows, dtype=torch.float32, device="cuda").reshape(w.n_pool_blocks, 1, w.block_size, 1)
+    v = rowid.expand(w.n_pool_blocks, w.n_kv_heads, w.block_size, w.head_dim).contiguous()
     out, lse = pkv.paged_attn_decode(d.q, d.k, v, d.table, d.lens, w.scale, mode="span", window=d.window)
     rows = np.array([oracle.physical_row(w.block_table[s], np.array([t[s]]), w.block_size)[0]
                      for s in range(w.n_seqs)])

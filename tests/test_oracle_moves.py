@@ -132,13 +132,15 @@ def test_p13_provenance_reads_out_row_ids():
     before = pool.copy()
     oracle.copy_cells([pool], ms.moves)
     assert np.array_equal(pool, before[prov])
-    # K and V pools of different widths move together
-    k = rng.standard_normal((ms.n_rows // 4, 4, 3))
-    v = rng.integers(0, 1 << 30, size=(ms.n_rows // 4, 4, 5))
+    # K and V pools in the block layout [blocks, kv heads, block_size, W],
+    # of different widths, move together: a row is one slot of every kv head
+    k = rng.standard_normal((ms.n_rows // 4, 2, 4, 3))
+    v = rng.integers(0, 1 << 30, size=(ms.n_rows // 4, 3, 4, 5))
     k0, v0 = k.copy(), v.copy()
     oracle.copy_cells([k, v], ms.moves)
-    assert np.array_equal(k.reshape(ms.n_rows, -1), k0.reshape(ms.n_rows, -1)[prov])
-    assert np.array_equal(v.reshape(ms.n_rows, -1), v0.reshape(ms.n_rows, -1)[prov])
+    r = np.arange(ms.n_rows)
+    for t, t0 in ((k, k0), (v, v0)):
+        assert np.array_equal(t[r // 4, :, r % 4], t0[prov // 4, :, prov % 4])
 
 
 def test_move_generator_shape():

@@ -33,11 +33,13 @@ def golden(name):
 
 
 def _bf_value(pool, fmt, row, kvh, d, hkv, hd):
+    """Element d of kv head kvh of pool row `row`; pool is [blocks, hkv, bs, W]."""
+    bs = pool.shape[2]
+    cell = pool[row // bs, kvh, row % bs]
     if fmt in ("f32", "f16"):
-        return float(pool.reshape(-1, hkv, hd)[row, kvh, d])
-    raw = pool.reshape(-1, pool.shape[-1])[row].tobytes()
-    blk = kvh * (hd // 32) + d // 32
-    off = blk * 34
+        return float(cell[d])
+    raw = cell.tobytes()
+    off = (d // 32) * 34
     (scale,) = struct.unpack("<e", raw[off : off + 2])
     (code,) = struct.unpack("<b", raw[off + 2 + d % 32 : off + 3 + d % 32])
     return scale * code
@@ -159,6 +161,7 @@ def test_golden_block_table_figure():
 
 def test_golden_q8_0_row_bytes():
     for c in golden("q8_0_row_bytes.json")["cases"]:
+        assert oracle.seg_bytes("q8_0", c["head_dim"]) == c["segment_bytes"]
         assert oracle.row_bytes("q8_0", c["n_kv_heads"], c["head_dim"]) == c["row_bytes"]
         assert wgen.q8_0_row_bytes(c["n_kv_heads"], c["head_dim"]) == c["row_bytes"]
     assert oracle.row_bytes("f16", 8, 128) == 2048
@@ -170,12 +173,12 @@ def _dense_to_paged(Kd, Vd, bs, perm):
     physical block perm[b] (p3's contiguous layout is perm = identity)."""
     L, hkv, hd = Kd.shape
     nb = -(-L // bs)
-    pool_k = np.full((len(perm), bs, hkv, hd), np.nan)
-    pool_v = np.full((len(perm), bs, hkv, hd), np.nan)
+    pool_k = np.full((len(perm), hkv, bs, hd), np.nan)
+    pool_v = np.full((len(perm), hkv, bs, hd), np.nan)
     for b in range(nb):
         n = min(bs, L - b * bs)
-        pool_k[perm[b], :n] = Kd[b * bs : b * bs + n]
-        pool_v[perm[b], :n] = Vd[b * bs : b * bs + n]
+        pool_k[perm[b], :, :n] = Kd[b * bs : b * bs + n].transpose(1, 0, 2)
+        pool_v[perm[b], :, :n] = Vd[b * bs : b * bs + n].transpose(1, 0, 2)
     table = np.array([perm[:nb]], dtype=np.int32)
     return pool_k, pool_v, table
 
@@ -276,12 +279,12 @@ def test_p5_closed_forms():
     # all value rows equal c: the output is c
     c = rng.standard_normal(hd)
     pv2 = pv.copy()
-    pv2[np.isfinite(pv2).all(axis=(2, 3))] = c
+    pv2[np.isfinite(pv2).all(axis=3)] = c
     out, _ = oracle.paged_decode(q, pk, pv2, "f32", "f32", table, np.array([L]), bs, 1, hd, 1.0)
     assert np.max(np.abs(out[0, 0] - c)) <= 1e-13
     # identical keys: uniform weights
     pk2 = pk.copy()
-    pk2[np.isfinite(pk2).all(axis=(2, 3))] = rng.standard_normal(hd)
+    pk2[np.isfinite(pk2).all(axis=3)] = rng.standard_normal(hd)
     out, _ = oracle.paged_decode(q, pk2, pv, "f32", "f32", table, np.array([L]), bs, 1, hd, 1.0)
     assert np.max(np.abs(out[0, 0] - Vd[:, 0].mean(0))) <= 1e-13
     # empty window: out 0, lse -inf
@@ -313,8 +316,8 @@ def test_p7_gqa_equals_mha_with_repeated_heads():
     out, lse = _oracle(w, q, k, v)
     g = w.group
     # repeat kv head h // g for every q head h: an MHA pool with hq kv heads
-    k2 = np.repeat(k, g, axis=2)
-    v2 = np.repeat(v, g, axis=2)
+    k2 = np.repeat(k, g, axis=1)
+    v2 = np.repeat(v, g, axis=1)
     out2, lse2 = oracle.paged_attention(q, w.q_seq(), w.query_pos(), k2, v2, "f32", "f32",
                                         w.block_table, w.seq_lens, w.block_size, w.n_q_heads,
                                         w.head_dim, w.scale, "causal")
@@ -330,13 +333,16 @@ def test_p8_nan_garbage_is_never_read(kfmt):
     assert not live.all()
     out, lse = _oracle(w, q, k, v)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    # the generator really poisoned the dead rows
-    vr = v.reshape(len(live), -1)
-    assert np.all(np.isnan(vr[~live])) and np.all(np.isfinite(vr[live]))
+    # the generator really poisoned the dead rows (cells of every kv head)
+    bs = w.block_size
+    rows = np.arange(len(live))
+    cells = v[rows // bs, :, rows % bs]
+    assert np.all(np.isnan(cells[~live])) and np.all(np.isfinite(cells[live]))
     # replacing the garbage by anything else changes nothing
-    v2 = v.copy().reshape(len(live), -1)
-    v2[~live] = 1e30
-    out2, _ = _oracle(w, q, k, v2.reshape(v.shape))
+    v2 = v.copy()
+    dead = rows[~live]
+    v2[dead // bs, :, dead % bs] = 1e30
+    out2, _ = _oracle(w, q, k, v2)
     assert np.array_equal(out, out2)
 
 
@@ -349,7 +355,8 @@ def test_p9_q8_0_decode_and_encoder_bound():
     x[0, 0, :32] = 0.0  # an all-zero block: scale 0, codes 0
     x[1, 1, 5] = 1e-3
     enc = wgen.encode_q8_0(torch.from_numpy(x), hkv, hd).numpy()
-    assert enc.shape == (n, oracle.row_bytes("q8_0", hkv, hd))
+    assert enc.shape == (n, hkv, oracle.seg_bytes("q8_0", hd))
+    enc = enc[:, :, None, :]  # a pool of n one-token blocks
     dec = oracle.decode_rows(enc, "q8_0", np.arange(n), hkv, hd)
     # decoding equals scale * code read with struct (Python's own binary16)
     for r in (0, 1, 77, 199):
@@ -363,7 +370,7 @@ def test_p9_q8_0_decode_and_encoder_bound():
     assert np.all(err <= bound)
     assert np.all(dec[0, 0, :32] == 0.0)
     # codes stay in [-127, 127] and the block max hits +-127
-    codes = enc[:, : hkv * 2 * 34].reshape(n, hkv * 2, 34)[:, :, 2:].view(np.int8)
+    codes = enc[:, :, 0, : 2 * 34].reshape(n, hkv * 2, 34)[:, :, 2:].view(np.int8)
     assert codes.min() >= -127 and codes.max() <= 127
     assert np.all(np.abs(codes.astype(np.int32)).max(-1)[1:] == 127)
 

@@ -16,6 +16,8 @@ from .gen import (  # noqa: F401
     materialize,
     encode_q8_0,
     q8_0_row_bytes,
+    q8_0_seg_bytes,
+    make_custom,
     referenced_rows,
     host_subset,
 )

@@ -41,11 +41,15 @@ KV_MAP_MAX_SPANS = 8
 INVALID_BLOCK = -1
 
 
-def q8_0_row_bytes(n_kv_heads: int, head_dim: int) -> int:
-    """Bytes of one q8_0 pool row: n_kv_heads * head_dim/32 blocks of
+def q8_0_seg_bytes(head_dim: int) -> int:
+    """Bytes of one token of one kv head in q8_0: head_dim/32 blocks of
     (f16 scale + 32 int8), rounded up to whole 4-byte words."""
-    raw = n_kv_heads * (head_dim // 32) * 34
-    return (raw + 3) // 4 * 4
+    return ((head_dim // 32) * 34 + 3) // 4 * 4
+
+
+def q8_0_row_bytes(n_kv_heads: int, head_dim: int) -> int:
+    """Bytes of one token (all kv heads) in q8_0."""
+    return n_kv_heads * q8_0_seg_bytes(head_dim)
 
 
 @dataclasses.dataclass
@@ -343,7 +347,8 @@ def referenced_rows(w: Workload) -> np.ndarray:
 
 
 def encode_q8_0(x, n_kv_heads: int, head_dim: int):
-    """Encode float32 rows [N, n_kv_heads, head_dim] as q8_0 bytes [N, row_bytes]:
+    """Encode float32 rows [N, n_kv_heads, head_dim] as q8_0 bytes
+    [N, n_kv_heads, seg_bytes]:
     per 32-element block d = amax/127 (f32), stored as f16 (round to nearest
     even), codes = clamp(round_half_even(x / d), -127, 127); amax = 0 gives
     d = 0 and zero codes.  Block = 2 bytes of little-endian f16 then 32 int8."""
@@ -360,50 +365,56 @@ def encode_q8_0(x, n_kv_heads: int, head_dim: int):
     d16 = d.to(torch.float16)
     blk = torch.cat([d16.contiguous().view(torch.uint8).reshape(n, n_kv_heads, nb, 2),
                      codes.view(torch.uint8)], dim=-1)
-    raw = blk.reshape(n, n_kv_heads * nb * 34)
-    rb = q8_0_row_bytes(n_kv_heads, head_dim)
-    if rb != raw.shape[1]:
-        pad = torch.zeros((n, rb - raw.shape[1]), dtype=torch.uint8, device=raw.device)
-        raw = torch.cat([raw, pad], dim=1)
+    raw = blk.reshape(n, n_kv_heads, nb * 34)
+    sb = q8_0_seg_bytes(head_dim)
+    if sb != raw.shape[2]:
+        pad = torch.zeros((n, n_kv_heads, sb - raw.shape[2]), dtype=torch.uint8, device=raw.device)
+        raw = torch.cat([raw, pad], dim=2)
     return raw.contiguous()
 
 
 def _gen_pool(w: Workload, fmt: str, gen, device, live_rows, chunk_rows: int):
+    """One pool in the block layout [n_blocks, n_kv_heads, block_size, W]
+    (W = head_dim values, or q8_0 segment bytes): inside a block, each kv
+    head's block_size token entries are contiguous.  Values are drawn one
+    token row [n_kv_heads, head_dim] at a time in pool row order."""
     import torch
 
     bs, hkv, hd = w.block_size, w.n_kv_heads, w.head_dim
-    n_rows = w.n_pool_blocks * bs
+    nblk = w.n_pool_blocks
     if fmt == "q8_0":
-        out = torch.empty((n_rows, q8_0_row_bytes(hkv, hd)), dtype=torch.uint8, device=device)
+        out = torch.empty((nblk, hkv, bs, q8_0_seg_bytes(hd)), dtype=torch.uint8, device=device)
     else:
         dt = torch.float32 if fmt == "f32" else torch.float16
-        out = torch.empty((n_rows, hkv, hd), dtype=dt, device=device)
+        out = torch.empty((nblk, hkv, bs, hd), dtype=dt, device=device)
     live = torch.from_numpy(live_rows).to(device)
-    for r0 in range(0, n_rows, chunk_rows):
-        r1 = min(n_rows, r0 + chunk_rows)
+    cb = max(1, chunk_rows // bs)  # whole blocks per chunk
+    for b0 in range(0, nblk, cb):
+        b1 = min(nblk, b0 + cb)
+        r0, r1 = b0 * bs, b1 * bs
         x = torch.randn((r1 - r0, hkv, hd), generator=gen, device=device, dtype=torch.float32)
         dead = ~live[r0:r1]
         if fmt == "q8_0":
-            enc = encode_q8_0(x, hkv, hd)
-            # poisoned rows: every block's scale is a quiet NaN (f16 0x7E00)
-            nanrow = enc.view(torch.uint8).reshape(r1 - r0, -1)
-            blk = nanrow[:, : hkv * (hd // 32) * 34].reshape(r1 - r0, hkv * (hd // 32), 34)
-            blk[dead, :, 0] = 0x00
-            blk[dead, :, 1] = 0x7E
-            out[r0:r1] = enc
+            enc = encode_q8_0(x, hkv, hd)  # [rows, hkv, seg]
+            # poisoned rows: every q8_0 block's scale is a quiet NaN (f16 0x7E00)
+            nb = hd // 32
+            blk = enc[:, :, : nb * 34].reshape(r1 - r0, hkv, nb, 34)
+            blk[dead, :, :, 0] = 0x00
+            blk[dead, :, :, 1] = 0x7E
+            enc[:, :, : nb * 34] = blk.reshape(r1 - r0, hkv, nb * 34)
+            rows = enc
         else:
             x[dead] = float("nan")
-            out[r0:r1] = x.to(out.dtype)
-    if fmt == "q8_0":
-        return out.reshape(w.n_pool_blocks, bs, -1)
-    return out.reshape(w.n_pool_blocks, bs, hkv, hd)
+            rows = x.to(out.dtype)
+        out[b0:b1] = rows.reshape(b1 - b0, bs, hkv, -1).permute(0, 2, 1, 3)
+    return out
 
 
 def materialize(w: Workload, device="cpu", chunk_rows: int = 1 << 16):
     """Draw (q, k_pool, v_pool) as torch tensors on ``device``.
 
-    q is [Nq, Hq, hd] in q_fmt; pools are [n_blocks, bs, Hkv, hd] (f32/f16) or
-    uint8 [n_blocks, bs, row_bytes] (q8_0).  Seeds: q from seed*1000+1, K from
+    q is [Nq, Hq, hd] in q_fmt; pools are [n_blocks, Hkv, bs, hd] (f32/f16)
+    or uint8 [n_blocks, Hkv, bs, seg_bytes] (q8_0).  Seeds: q from seed*1000+1, K from
     seed*1000+2, V from seed*1000+3, each on its own generator."""
     import torch
 
