@@ -18,12 +18,20 @@ resident in HBM.  Prints one JSON line:
   workload on this host.
 
 Other workloads (for the record; the default is the headline): decode1,
-decode2, decode5, prefill4, copy5b.
+decode2, decode5, prefill4, copy5b; and calib, a plain device copy of known
+size used to scale the HBM byte counters.
+
+Counter summary (turns two rocprofv3 --pmc runs, FETCH_SIZE then WRITE_SIZE,
+of a workload and of the calibration copy into bytes per launch):
+
+    python bench.py --pmc-summary KERNEL FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -31,7 +39,14 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
+CALIB_BYTES = 4 << 30  # bytes read and bytes written by one calibration copy
+# Sources that determine the decode split kernel's code; a stored counter
+# summary only applies while their hash is unchanged.
+DECODE_SOURCES = ("include/pkv.h", "paged_kv_cache_table_amd/csrc/pkv_internal.hpp",
+                  "paged_kv_cache_table_amd/csrc/decode_impl.hpp", "paged_kv_cache_table_amd/csrc/decode_f16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_7b_class.traffic.json")
 MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + queries/s"
 
@@ -107,6 +122,75 @@ def cpu_baseline_decode(w, d, budget_s=12.0):
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "queries_per_s": round(len(seqs) / t_total, 4),
     }
+
+
+def sources_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the decode split kernel from the committed
+    counter summary, or None if absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sources_hash(DECODE_SOURCES):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def _pmc_mean(path, kernel_substr, counter):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr!r} in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(kernel, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of `kernel`, each scaled by
+    the factor that maps the same counter to the known bytes of the
+    calibration copy."""
+    f_kib, nf = _pmc_mean(fetch_csv, kernel, "FETCH_SIZE")
+    w_kib, nw = _pmc_mean(write_csv, kernel, "WRITE_SIZE")
+    cf_kib, _ = _pmc_mean(cal_fetch_csv, "copy", "FETCH_SIZE")
+    cw_kib, _ = _pmc_mean(cal_write_csv, "copy", "WRITE_SIZE")
+    f_scale = CALIB_BYTES / (cf_kib * 1024)
+    w_scale = CALIB_BYTES / (cw_kib * 1024)
+    out = {
+        "kernel": kernel,
+        "sources_sha256": sources_hash(DECODE_SOURCES),
+        "fetch_kib_per_dispatch": round(f_kib, 1), "fetch_dispatches": nf,
+        "write_kib_per_dispatch": round(w_kib, 1), "write_dispatches": nw,
+        "calib_fetch_kib": round(cf_kib, 1), "calib_write_kib": round(cw_kib, 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "traffic_bytes_per_launch": int(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale),
+    }
+    print(json.dumps(out, indent=2))
+    return 0
+
+
+def run_calib(args):
+    import torch
+
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"workload": "calib", "bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES,
+            "ms_per_copy": round(ms, 4), "GBps_read_plus_write": round(2 * CALIB_BYTES / (ms * 1e-3) / 1e9, 1)}
 
 
 def run_decode(cfg, args):
@@ -199,7 +283,7 @@ def run_decode(cfg, args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic() if cfg == 3 and not args.split else None,
             "algorithmic_bytes": int(alg),
         },
     }
@@ -212,11 +296,14 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode3",
-                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b"])
+                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "calib"])
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
     ap.add_argument("--split", type=int, default=0, help="decode split size in tokens (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args(argv)
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(sequences shard across GPUs with no exchange, so per-GPU throughput is the figure).",
@@ -227,6 +314,9 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.workload == "calib":
+        print(json.dumps(run_calib(args)), flush=True)
+        return 0
     if args.workload.startswith("decode"):
         res, w, d = run_decode(int(args.workload[-1]), args)
         if not args.no_cpu_baseline:

@@ -136,11 +136,12 @@ pkv_status check_attn(const pkv_shape* sh, int mode, int n_runs, const void* win
 }
 
 // Decode split size: the largest of 64, 32, 16, 8, 4 blocks that still gives
-// enough work items (an upper bound from the table width) to spread over the
-// GPU with a short tail.  Depends on the shape only.
+// enough work items (an upper bound from the table width) to keep every CU
+// busy: long splits write fewer partials for the merge, short ones shorten
+// the tail.  Depends on the shape only.
 int auto_split(const pkv_shape* sh, int runs) {
   const int64_t ctx = (int64_t)sh->max_blocks_per_seq * sh->block_size;
-  const int64_t target = 32768;
+  const int64_t target = 3072;
   for (int nb : {64, 32, 16, 8}) {
     const int64_t sp = (int64_t)nb * sh->block_size;
     const int64_t items = (int64_t)sh->n_seqs * sh->n_kv_heads * runs * ((ctx + sp - 1) / sp);
