@@ -27,13 +27,14 @@ struct AttnArgs {
   const int32_t* q_pos;     // prefill [n_q_total]
   float* out;
   float* lse;
-  float* part_o;   // decode partials [S][n_slots][Hq][HD]
-  float* part_ml;  // decode partials [S][n_slots][Hq][2] = (max, sum)
+  float* part_o;   // decode partials [S][n_slots][Hq][HD]; prefill [Nq][Hq][nch][HD]
+  float* part_ml;  // decode partials [S][n_slots][Hq][2] = (max, sum); prefill [Nq][Hq][nch][2]
   int32_t* err;    // checked mode: count of bad block ids
   int32_t n_seqs, n_q_heads, n_kv_heads, n_pool_blocks, max_blocks, block_size;
   int32_t mode, n_runs;  // n_runs = runs per sequence (1 unless kv_map)
   int32_t split, nspl;   // decode: tokens per split, split slots per run
   int32_t n_q_total, max_q;
+  int32_t nch;           // prefill: chunks each workgroup's window is split into
   // Pool layout [n_blocks][n_kv_heads][block_size][seg]: seg = bytes of one
   // token of one kv head; a block is n_kv_heads * block_size * seg bytes.
   int64_t k_seg_bytes, v_seg_bytes, k_block_bytes, v_block_bytes;
@@ -192,7 +193,7 @@ hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
 // Prefill: workspace bytes a call needs (a multiple of 256, the last 256
 // bytes hold the checked-mode error word; 0 if none) and whether a kernel
-// exists for the tuple; then the launch.
+// exists for the tuple; then the launch (a.part_o = the workspace base).
 size_t prefill_workspace(const AttnArgs& a, int combo, int hd, int bs, int g, bool* found);
 hipError_t launch_prefill(const AttnArgs& a, int combo, int hd, int bs, int g, hipStream_t st,
                           bool* found);
