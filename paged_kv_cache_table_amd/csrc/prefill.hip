@@ -8,33 +8,42 @@
 // s and q head h, softmax attention over the window positions t of s with
 // t < min(seq_len_s, q_pos_j + 1), t not in a hole.
 //
-// Work decomposition.  A workgroup (4 waves) takes one kv head, a block of
-// consecutive queries of one sequence (128 rows = (query, q head of the
-// GQA group) pairs, 32 per wave in two 16-row tiles) and one of nch chunks
-// of the window: the window's runs, clipped to [0, min(seq_len, largest
-// causal limit of the rows)), are seen as one concatenated index space cut
-// into nch equal chunks.  With nch > 1 each workgroup writes (max, sum,
-// unnormalised output) per row and a merge kernel combines them with the
-// log-sum-exp rule; with nch = 1 the output is written directly.  Workgroups
-// that share a chunk's K/V are numbered so that they land on the same XCD
-// (consecutive task numbers map to one XCD's share of the grid).
+// Work decomposition.  A workgroup (8 waves, two per SIMD) takes one kv
+// head, a block of consecutive queries of one sequence (rows = (query, q head
+// of the GQA group) pairs, 16 * RT per wave) and one of nch chunks of the
+// window.  Each run of the window, clipped to [0, min(seq_len, largest causal
+// limit of the rows)), is covered by the T-aligned tiles that meet it; the
+// runs' tiles in order form one list that is cut into nch equal chunks.  With
+// nch > 1 each workgroup writes (max, sum, unnormalised output) per row and a
+// merge kernel combines them with the log-sum-exp rule; with nch = 1 the
+// output is written directly.  Workgroups that share a chunk's K/V are
+// numbered so that they land on the same XCD.
 //
-// Per tile of T window positions (never crossing a run): K is staged in LDS
-// row-major (f16, or q8_0 codes widened to f16 exactly plus one f32 scale per
-// (position, 32-wide block)); V row-major.  Tiles are double-buffered: the
-// loads of the next tile are in flight while the current one is computed,
-// and the block-table entries are fetched two tiles ahead.  Scores are
-// computed transposed, S^T = K Q^T, so each lane holds T/4 scores of one row
-// (positions g + 4j of the tile for lane group g): the row's running max and
-// sum live in the lane and the rounded probabilities are already the B
-// operand of O^T = V^T P^T, whose A operand gathers one head_dim column of V
-// over positions g + 4j with 16-bit LDS reads (rows g and g + 1 are 8 banks
-// apart, so the four lane groups never collide).  For q8_0 K every 32-wide
-// head_dim block is one MFMA whose result is scaled by that position's block
-// scale before it is added: the dequantised value scale * code is never
-// rounded to f16.  Positions outside the run, in a hole or past a row's
-// causal limit get probability 0 by selection; a tile with none of these
-// skips the masking.  Staged K/V of such positions are zeros.
+// Data movement.  A tile is T/BS whole blocks.  Each wave copies its T/8
+// positions of a tile (which lie in one block: one scalar base address per
+// tile, fixed per-lane offsets) straight from HBM into LDS
+// (global_load_lds: no registers in between), two tiles ahead of the
+// compute, into a ring of three tile slots; it then waits for its own copies
+// only (vmcnt) and prepares its rows (V rows of positions that are not
+// visible zeroed; a q8_0 value x = scale * code, exact in f32, split into
+// hi = f16(x) and lo = f16(x - hi), which represent x exactly for every f16
+// scale and int8 code), so one barrier per tile suffices.  f16 rows are
+// stored row-major with their 16-byte chunks XOR-swizzled by the row index,
+// which keeps both the score-operand reads and the transposing V reads free
+// of bank conflicts.
+//
+// Compute.  Scores are computed transposed, S^T = K Q^T, so each lane holds
+// T/4 scores of one row (positions 16 st + 4 g + i): the row's running max
+// and sum live in the lane and the rounded probabilities are already the B
+// operand of O^T = V^T P^T.  Its A operand (a head_dim column of V over those
+// positions) comes from ds_read_b64_tr_b16: within each 16-lane group, lane i
+// receives element i % 4 of the 4 halves that lane 4 e + i / 4 addressed, as
+// element e.  For q8_0 K the scores are K_hi Q^T + K_lo Q^T: the products are
+// exact in f32, so the dequantised value is never rounded.  The row sums of
+// the rounded probabilities come from one more MFMA per PV step whose A
+// operand is all ones (the same rounded values as the numerator).  Positions
+// outside the run, in a hole or past a row's causal limit score -inf; a tile
+// with none of these skips the masking.
 #include "pkv_internal.hpp"
 
 namespace pkv {
@@ -42,36 +51,106 @@ namespace pkv {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-constexpr int kPWaves = 4;      // waves per workgroup
-constexpr int kRowTiles = 2;    // 16-row tiles per wave
-constexpr int kRowsWG = kPWaves * kRowTiles * 16;
+constexpr int kPWaves = 8;          // waves per workgroup (two per SIMD)
+constexpr int kRing = 3;            // LDS tile slots: copies run two tiles ahead
 constexpr float kEmptyMax = -1e30f;
-constexpr int kTargetTasks = 1024;  // workgroups the chunking aims for
-constexpr int kMaxChunks = 16;
 constexpr float kLazyMax = 8.0f;    // log2 growth of a row max that forces a rescale
+constexpr int kTargetTasks = 512;   // workgroups the chunking aims for
+constexpr int kMaxChunks = 16;
 
-// V is stored for the PV A operand: word i of (32-position half kh, lane
-// group g, column d) holds the f16 pair (V[32 kh + g + 8 i][d],
-// V[32 kh + g + 8 i + 4][d]), the four words of a (kh, g, d) are one 16-byte
-// read, and every eighth column is followed by a 16-byte gap so that the
-// staging writes (16 columns apart) spread over the banks.
-template <int HD, int T>
-struct __attribute__((aligned(16))) PrefillSmem {
-  static constexpr int KLD = HD + 8;         // K row stride (halfs): 16-byte rows, 4 banks apart
-  static constexpr int VDP = HD + HD / 8;    // padded columns per (kh, g)
-  _Float16 k[2][T][KLD];
-  uint32_t v[2][T / 32][4][VDP][4];
-  float ks[2][HD / 32][T];  // q8_0 block scales, in the order the score lanes read them
-  int32_t id[2][T];         // physical block of each staged position, -1 = not visible
-  int32_t lim_max;          // largest causal limit of the workgroup's rows
+// Tile shape per head_dim: positions per tile and 16-row tiles per wave.
+__host__ __device__ constexpr int tile_of(int hd) { return hd <= 128 ? 64 : 32; }
+__host__ __device__ constexpr int row_tiles_of(int hd) { return hd <= 128 ? 2 : 1; }
+__host__ __device__ constexpr int rows_per_wg(int hd) { return kPWaves * row_tiles_of(hd) * 16; }
+
+template <int HD>
+struct PGeom {
+  static constexpr int T = tile_of(HD);                      // window positions per tile
+  static constexpr int RT = row_tiles_of(HD);                // 16-row tiles per wave
+  static constexpr int PPW = T / kPWaves;                    // positions each wave copies and prepares
+  static constexpr int KS = HD / 32;                         // q8_0 blocks / MFMA k-steps
+  static constexpr int CHR = HD / 8;                         // 16-byte chunks per f16 row
+  static constexpr int SWZ = (CHR < 16 ? CHR : 16) - 1;      // chunk XOR mask
+  static constexpr int ROWB = HD * 2;                        // bytes per f16 row
+  static constexpr int TILEB = T * ROWB;                     // bytes per f16 tile
+  static constexpr int NV = PPW * CHR / 64;                  // 16-byte copies per wave per f16 tile
+  static constexpr int SEG8 = (KS * 34 + 3) / 4 * 4;         // bytes per q8_0 segment
+  static constexpr int RAWW = PPW * SEG8;                    // bytes of a wave's q8_0 rows
+  static constexpr int CPW = RAWW / 16;                      // their 16-byte chunks
+  static constexpr int NRW = (CPW + 63) / 64;                // 16-byte copies per wave per q8_0 tile
+  static constexpr int UPR = HD / 16;                        // q8_0 half blocks per position (even)
+  static constexpr int NQ8 = (PPW * UPR + 63) / 64;          // half blocks per lane
+  static_assert(PPW * CHR % 64 == 0 && RAWW % 16 == 0, "copy shapes");
 };
+
+template <int HD, bool KQ8>
+struct __attribute__((aligned(16))) PrefillSmem {
+  using Gm = PGeom<HD>;
+  unsigned char v[kRing][Gm::TILEB];                                  // V tiles
+  // K tiles: f16 as copied, or q8_0 widened into the pair (hi, lo) of f16
+  // tiles with hi + lo == scale * code exactly
+  unsigned char k[KQ8 ? 2 : kRing][KQ8 ? 2 : 1][Gm::TILEB];
+  unsigned char raw[KQ8 ? kRing : 1][KQ8 ? kPWaves * Gm::RAWW : 16];  // q8_0 tiles as stored
+  int32_t lim_max;                                                    // largest causal limit of the rows
+};
+
+// Byte offset of 16-byte chunk c of row r in an f16 tile.
+template <int HD>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * PGeom<HD>::ROWB + ((c ^ (r & PGeom<HD>::SWZ)) << 4);
+}
 
 __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// HBM -> LDS copies (global_load_lds): each lane's bytes land at lds + lane *
+// size.  Issued as inline assembly so that the compiler, which cannot tell
+// which LDS reads they may alias, adds no waits of its own; the kernel waits
+// for them explicitly (wait_vm) before a barrier publishes the data.  M0 is
+// named as clobbered; nothing else in this file keeps a value in M0 (the
+// generated code only writes it right before these copies).
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes from base + off (base wave-uniform, off per lane) to lds + 16 * lane.
+// base and lds are read through readfirstlane so that they are scalar
+// registers whatever the compiler can prove about their uniformity.
+__device__ __forceinline__ void copy16_to_lds(const unsigned char* base, uint32_t off, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t bu = ((uint64_t)(uint32_t)uni((int32_t)(b >> 32)) << 32) | (uint32_t)uni((int32_t)(uint32_t)b);
+  const uint32_t lu = (uint32_t)uni((int32_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"((const unsigned char*)(uintptr_t)bu), "s"(lu)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (GFX9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups): each
+// swap exchanges the odd rows (or the upper half) of one copy of the value
+// with the even rows (lower half) of another copy, so the two registers then
+// hold the value of the lane and of its partner.  Written as inline assembly
+// with both registers as outputs: the compiler's builtin for these swaps
+// returns the first register for both results.
+__device__ __forceinline__ float max_over_groups(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 0\n\tv_max_f32 %0, %0, %1" : "+v"(a), "+v"(b));
+  b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 0\n\tv_max_f32 %0, %0, %1" : "+v"(a), "+v"(b));
+  return a;
+}
 
 // Four int8 codes (one dword) to four exactly equal f16 values: with the sign
 // bit flipped a code is u = code + 128 in [0, 255], the f16 with bits
@@ -85,64 +164,114 @@ __device__ __forceinline__ void codes_to_f16(uint32_t x, half2_t& lo, half2_t& h
   hi = __builtin_bit_cast(half2_t, phi) - bias;
 }
 
-// This workgroup's walk over the window: runs in order, each clipped to
-// [0, lim), as one concatenated index space of which [va, vend) is ours.
-// All fields are wave-uniform.
+// Run r of sequence s clipped to [0, limit) (same rule as run_range; reads
+// the window through a pointer the compiler may load with scalar loads).
+__device__ inline void run_bounds(const AttnArgs& a, const int32_t* __restrict__ window, int s, int r,
+                                  int32_t limit, int32_t& lo, int32_t& hi) {
+  int64_t x0 = 0, x1 = 0;
+  if (a.mode == PKV_WIN_CAUSAL) {
+    x1 = limit;
+  } else if (a.mode == PKV_WIN_SPAN) {
+    x0 = window[2 * s];
+    x1 = window[2 * s + 1];
+  } else {
+    const int32_t* wr = window + ((int64_t)s * a.n_runs + r) * 2;
+    const int64_t c = wr[0], n = wr[1];
+    if (n > 0) {
+      x0 = c;
+      x1 = c + n;
+    }
+  }
+  if (x0 < 0) x0 = 0;
+  if (x1 > limit) x1 = limit;
+  if (x1 < x0) x1 = x0;
+  lo = uni((int32_t)x0);
+  hi = uni((int32_t)x1);
+}
+
+// This workgroup's walk over the window.  Each run, clipped to [0, lim), is
+// covered by the T-aligned tiles that meet it (its first and last tile may be
+// partial); the runs' tiles in order form one list of which the workgroup
+// takes [ta, tb).  All fields are wave-uniform.
 struct Walk {
   int32_t r;       // current run (== n_runs: finished)
-  int32_t vb;      // index-space offset of run r
-  int32_t len;     // clipped length of run r
-  int32_t lo, hi;  // our positions of run r
-  int32_t t0;      // current tile start
+  int32_t lo, hi;  // run r clipped
+  int32_t k, n;    // tile k of the run's n tiles
+  int32_t left;    // tiles left in the chunk
 };
 
-__device__ inline void walk_seek(const AttnArgs& a, int s, int32_t lim, int32_t va, int32_t vend,
-                                 Walk& w) {
-  while (w.r < a.n_runs) {
-    int32_t ra, rb;
-    run_range(a, s, w.r, lim, ra, rb);
-    ra = uni(ra);
-    rb = uni(rb);
-    w.len = rb - ra;
-    const int32_t v0 = va > w.vb ? va : w.vb;
-    const int32_t v1 = vend < w.vb + w.len ? vend : w.vb + w.len;
-    if (v0 < v1) {
-      w.lo = ra + (v0 - w.vb);
-      w.hi = ra + (v1 - w.vb);
-      w.t0 = w.lo;
+template <int T>
+struct WalkCtx {
+  const AttnArgs& a;
+  const int32_t* __restrict__ window;
+  int s;
+  int32_t lim;
+
+  __device__ int32_t tiles(int r, int32_t& lo, int32_t& hi) const {
+    run_bounds(a, window, s, r, lim, lo, hi);
+    return hi > lo ? (hi + T - 1) / T - lo / T : 0;
+  }
+  // position the walk on tile ta of the list, ending at tb
+  __device__ void start(Walk& w, int32_t ta, int32_t tb) const {
+    w.left = tb - ta;
+    w.r = a.n_runs;
+    if (w.left <= 0) return;
+    int32_t before = 0;
+    for (int r = 0; r < a.n_runs; ++r) {
+      int32_t lo, hi;
+      const int32_t n = tiles(r, lo, hi);
+      if (ta < before + n) {
+        w.r = r;
+        w.lo = lo;
+        w.hi = hi;
+        w.n = n;
+        w.k = ta - before;
+        return;
+      }
+      before += n;
+    }
+  }
+  __device__ void next(Walk& w) const {
+    if (w.r >= a.n_runs) return;
+    if (--w.left <= 0) {
+      w.r = a.n_runs;
       return;
     }
-    w.vb += w.len;
-    ++w.r;
+    if (++w.k < w.n) return;
+    do {
+      ++w.r;
+      w.k = 0;
+      w.n = w.r < a.n_runs ? tiles(w.r, w.lo, w.hi) : 0;
+    } while (w.r < a.n_runs && w.n == 0);
   }
-}
+  __device__ int32_t t0(const Walk& w) const { return (w.lo / T + w.k) * T; }
+};
 
-template <int T>
-__device__ inline void walk_next(const AttnArgs& a, int s, int32_t lim, int32_t va, int32_t vend,
-                                 Walk& w) {
-  if (w.r >= a.n_runs) return;
-  w.t0 += T;
-  if (w.t0 < w.hi) return;
-  w.vb += w.len;
-  ++w.r;
-  walk_seek(a, s, lim, va, vend, w);
-}
+// One staged tile (wave-uniform): it starts at t0 (a multiple of T) and vm
+// has bit p set when position t0 + p is visible (inside the run, not in a
+// hole).
+struct TileD {
+  int32_t t0;
+  uint64_t vm;
+};
 
-template <int HD, int BS, int G, bool KQ8, int T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 128 ? 2 : 1, HD <= 128 ? 2 : 1)))
-void prefill_kernel(AttnArgs a, int32_t n_tasks, int32_t nqb) {
-  constexpr int KS = HD / 32;                     // MFMA k-steps over head_dim
+template <int HD, int BS, int G, bool KQ8>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t* __restrict__ window,
+                    const unsigned char* __restrict__ kpool, const unsigned char* __restrict__ vpool,
+                    int32_t n_tasks, int32_t nqb) {
+  using Gm = PGeom<HD>;
+  constexpr int T = Gm::T;
+  constexpr int RT = Gm::RT;
+  constexpr int PPW = Gm::PPW;
+  constexpr int KS = Gm::KS;                      // MFMA k-steps over head_dim
   constexpr int DT = HD / 16;                     // 16-wide head_dim tiles of the output
-  constexpr int CHR = HD / 8;                     // 16-byte chunks per f16 row
-  constexpr int QPB = kRowsWG / G;                // queries per workgroup
-  constexpr int NKH = T / 32;                     // 32-position halves of a tile
-  constexpr int NJ = T / 4;                       // scores per lane per row tile
-  constexpr int NCH = (T * CHR + 255) / 256;      // f16 row chunks per thread
-  constexpr int UPR = HD / 16;                    // q8_0 half blocks per row
-  constexpr int NQ8 = (T * UPR + 255) / 256;      // q8_0 half blocks per thread
-  constexpr int NID = (T + BS - 1) / BS + 1;      // table entries one tile can touch
-  static_assert(T == 32 || T == 64, "tile");
-  __shared__ __attribute__((aligned(16))) PrefillSmem<HD, T> sm;
+  constexpr int QPB = rows_per_wg(HD) / G;        // queries per workgroup
+  constexpr int NKH = T / 32;                     // 32-position halves (PV k-steps)
+  constexpr int NID = T / BS;                     // blocks per tile (tiles are T-aligned)
+  constexpr int NDMA = KQ8 ? Gm::NV + Gm::NRW : 2 * Gm::NV;  // copies per wave per tile
+  static_assert(BS == 16 || BS == 32, "a tile is whole blocks and a wave's positions one block");
+  __shared__ PrefillSmem<HD, KQ8> sm;
 
   // ---- task: ((s * Hkv + kvh) * nch + c) * nqb + qb, XCD-major numbering
   const int32_t n8 = (n_tasks + 7) >> 3;
@@ -155,7 +284,7 @@ void prefill_kernel(AttnArgs a, int32_t n_tasks, int32_t nqb) {
   const int kvh = rest % a.n_kv_heads;
   const int s = rest / a.n_kv_heads;
 
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, n16 = l & 15;
+  const int t = threadIdx.x, w = uni(t >> 6), l = t & 63, g = l >> 4, n16 = l & 15;
   int q0 = a.cu_q[s], q1 = a.cu_q[s + 1];
   q0 = q0 < 0 ? 0 : (q0 > a.n_q_total ? a.n_q_total : q0);
   q1 = q1 < q0 ? q0 : (q1 > a.n_q_total ? a.n_q_total : q1);
@@ -165,17 +294,17 @@ void prefill_kernel(AttnArgs a, int32_t n_tasks, int32_t nqb) {
   const int j1 = j0 + QPB < q1 ? j0 + QPB : q1;
   const int32_t L = clamp_seq_len(a.seq_lens[s], a.max_blocks, BS);
 
-  // ---- rows of this lane: row tile rt covers rows w*32 + rt*16 + n16
-  int jq[kRowTiles], hq[kRowTiles];
-  bool rok[kRowTiles];
-  int32_t lim[kRowTiles];
-  half8_t qf[kRowTiles][KS];
+  // ---- rows of this lane: row tile rt covers rows (w * RT + rt) * 16 + n16
+  int jq[RT], hq[RT];
+  bool rok[RT];
+  int32_t lim[RT];
+  half8_t qf[RT][KS];
   if (t == 0) sm.lim_max = 0;
   __syncthreads();
   int32_t lmin = 0x7fffffff;
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int rr = w * 32 + rt * 16 + n16;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rr = (w * RT + rt) * 16 + n16;
     jq[rt] = j0 + rr / G;
     hq[rt] = rr % G;
     rok[rt] = rr < QPB * G && jq[rt] < j1;
@@ -199,356 +328,362 @@ void prefill_kernel(AttnArgs a, int32_t n_tasks, int32_t nqb) {
   }
   // smallest causal limit over the wave's rows (wave-uniform)
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int32_t o = __shfl_xor(lmin, m, 64);
+  for (int mm = 1; mm < 64; mm <<= 1) {
+    const int32_t o = __shfl_xor(lmin, mm, 64);
     lmin = o < lmin ? o : lmin;
   }
   const int32_t lim_min_w = uni(lmin);
   __syncthreads();
   const int32_t lim_max = uni(sm.lim_max);
 
-  // ---- this workgroup's chunk of the window
-  int32_t W = 0;
+  // ---- this workgroup's chunk of the window's tile list
+  const WalkCtx<T> wx{a, window, s, lim_max};
+  int32_t NT = 0;
   for (int r = 0; r < a.n_runs; ++r) {
-    int32_t ra, rb;
-    run_range(a, s, r, lim_max, ra, rb);
-    W += rb - ra;
+    int32_t lo, hi;
+    NT += wx.tiles(r, lo, hi);
   }
-  W = uni(W);
-  const int32_t chl = ((W + a.nch - 1) / a.nch + T - 1) / T * T;
-  const int32_t va = c * chl, vend = va + chl < W ? va + chl : W;
+  const int32_t per = (NT + a.nch - 1) / a.nch;
+  const int32_t ta = c * per, tb = ta + per < NT ? ta + per : NT;
 
-  float m[kRowTiles], lsum[kRowTiles];
-  float4_t o[kRowTiles][DT];
+  float m[RT];
+  float4_t o[RT][DT + 1];  // o[rt][DT]: the row's sum of probabilities
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     m[rt] = kEmptyMax;
-    lsum[rt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt <= DT; ++dt) o[rt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const unsigned char* kbase = a.k_pool + (int64_t)kvh * BS * a.k_seg_bytes;
-  const unsigned char* vbase = a.v_pool + (int64_t)kvh * BS * a.v_seg_bytes;
-  const bool count_bad = kvh == 0 && qb == 0 && t == 0;
+  const unsigned char* kbase = kpool + (int64_t)kvh * BS * a.k_seg_bytes;
+  const unsigned char* vbase = vpool + (int64_t)kvh * BS * a.v_seg_bytes;
+  const int32_t* trow = table + (int64_t)s * a.max_blocks;
   // |scale| * log2(e), kept above 0 so that a hidden score (-inf) always
   // gives p = 0 (a zero scale then weighs every visible position equally)
   const float mul = fmaxf(fabsf(a.score_mul), 1e-30f);
+  const int pw0 = w * PPW;    // first position this wave copies and prepares
+  const int wblk = pw0 / BS;  // the tile block holding this wave's positions
+  int32_t bad = 0;            // out-of-range table entries seen (checked mode)
 
-  // table entries of the blocks a tile touches, loaded raw (wave-uniform
-  // addresses) a tile before they are used, and checked when used
-  auto load_ids = [&](const Walk& x, int32_t (&ids)[NID]) {
-    const int32_t b0 = x.t0 / BS;
-    const int32_t te = x.t0 + T < x.hi ? x.t0 + T : x.hi;
-    const int32_t blast = (te - 1) / BS;
-    const int32_t* row = a.table + (int64_t)s * a.max_blocks;
+  // per-lane byte offsets inside a (block, kv head) region: tile-invariant
+  uint32_t voff[Gm::NV], qoff[KQ8 ? Gm::NRW : 1];
 #pragma unroll
-    for (int i = 0; i < NID; ++i) ids[i] = b0 + i <= blast ? row[b0 + i] : -1;
+  for (int i = 0; i < Gm::NV; ++i) {
+    const int uu = i * 64 + l;
+    const int r = pw0 + uu / Gm::CHR, pc = uu % Gm::CHR;
+    voff[i] = (uint32_t)((r & (BS - 1)) * a.v_seg_bytes + ((pc ^ (r & Gm::SWZ)) << 4));
+  }
+  if constexpr (KQ8) {
+#pragma unroll
+    for (int i = 0; i < Gm::NRW; ++i) qoff[i] = (uint32_t)((pw0 & (BS - 1)) * Gm::SEG8 + (i * 64 + l) * 16);
+  }
+
+  // block ids of a tile (raw table entries; -1 past the table)
+  auto load_ids = [&](const Walk& x, int32_t (&ids)[NID]) {
+    const int32_t b0 = wx.t0(x) / BS;
+#pragma unroll
+    for (int i = 0; i < NID; ++i) ids[i] = b0 + i < a.max_blocks ? trow[b0 + i] : -1;
   };
-  const bool checked = (a.flags & PKV_FLAG_CHECKED) && a.err && kvh == 0 && qb == 0;
-  auto check_ids = [&](const Walk& x, int32_t (&ids)[NID]) {
-    const int32_t b0 = x.t0 / BS;
-    int bad = 0;
+  // tile descriptor; ids become checked block ids (-1: hole or out of range)
+  auto make_tile = [&](const Walk& x, int32_t (&ids)[NID]) {
+    TileD d;
+    d.t0 = wx.t0(x);
+    const int32_t lo = (x.lo > d.t0 ? x.lo : d.t0) - d.t0;
+    const int32_t hi = (x.hi < d.t0 + T ? x.hi : d.t0 + T) - d.t0;
+    uint64_t vm = (hi >= 64 ? ~0ull : (1ull << hi) - 1ull) & ~((1ull << lo) - 1ull);
 #pragma unroll
     for (int i = 0; i < NID; ++i) {
       const int32_t id = uni(ids[i]);
-      const bool out = id < -1 || id >= a.n_pool_blocks;
-      // count a bad entry once: in the tile holding the block's first visible position
-      if (out && ((b0 + i) * BS >= x.t0 || x.t0 == x.lo)) ++bad;
-      ids[i] = (id < 0 || out) ? -1 : id;
+      const bool ok = id >= 0 && id < a.n_pool_blocks;
+      const uint64_t bm = ((1ull << BS) - 1ull) << (i * BS);
+      if (!ok && id != -1 && (vm & bm)) ++bad;
+      if (!ok) vm &= ~bm;
+      ids[i] = ok ? id : -1;
     }
-    if (checked && bad) {
-      if (t == 0) atomicAdd(a.err, bad);
-    }
+    d.vm = vm;
+    return d;
   };
 
-  // staged data of one tile, in registers between load and LDS store
-  constexpr int NVU = (T / 2 * CHR + 255) / 256;  // V units (position pair, 8 columns) per thread
-  uint4 vr[NVU][2];
-  uint4 kr[KQ8 ? 1 : NCH];
-  uint32_t qw[KQ8 ? NQ8 : 1][5];
-  int32_t vid[NVU][2], kid[KQ8 ? NQ8 : NCH];
-
-  auto pick = [&](const int32_t (&ids)[NID], int32_t i) {
-    int32_t id = ids[0];
+  // copy this wave's positions of a tile into LDS slot sl (no waiting); a
+  // block that is a hole copies block 0, which always exists
+  auto issue = [&](int sl, const int32_t (&ids)[NID]) {
+    const int64_t blk = ids[wblk] >= 0 ? ids[wblk] : 0;
+    const unsigned char* vb = vbase + blk * a.v_block_bytes;
+    const unsigned char* kb = kbase + blk * a.k_block_bytes;
 #pragma unroll
-    for (int k = 1; k < NID; ++k) id = i == k ? ids[k] : id;
-    return id;
-  };
-  // Loads are unconditional (a position that is not visible reads block 0,
-  // which always exists, and is zeroed when stored) so that no lane-divergent
-  // branch sits between the loads and the compute they overlap.  A lane's
-  // address is one of the tile's (at most NID) block bases plus a 32-bit
-  // offset inside the block.
-  auto stage_issue = [&](const Walk& x, const int32_t (&ids)[NID]) {
-    const int32_t te = x.t0 + T < x.hi ? x.t0 + T : x.hi;
-    const int32_t b0 = x.t0 / BS;
-    // block bases (wave-uniform); a hole reads block 0
-    const unsigned char* vb[NID];
-    const unsigned char* kb[NID];
-#pragma unroll
-    for (int i = 0; i < NID; ++i) {
-      const int64_t idc = ids[i] >= 0 ? ids[i] : 0;
-      vb[i] = vbase + idc * a.v_block_bytes;
-      kb[i] = kbase + idc * a.k_block_bytes;
+    for (int i = 0; i < Gm::NV; ++i) {
+      copy16_to_lds(vb, voff[i], lds_addr(&sm.v[sl][pw0 * Gm::ROWB + i * 1024]));
+      if constexpr (!KQ8) copy16_to_lds(kb, voff[i], lds_addr(&sm.k[sl][0][pw0 * Gm::ROWB + i * 1024]));
     }
-    auto sel = [&](const unsigned char* const (&bases)[NID], int32_t bi) {
-      const unsigned char* p = bases[0];
+    if constexpr (KQ8) {
 #pragma unroll
-      for (int k = 1; k < NID; ++k) p = bi == k ? bases[k] : p;
-      return p;
-    };
-#pragma unroll
-    for (int e = 0; e < NVU; ++e) {
-      const int uv = t + 256 * e;
-      const int pr = uv / CHR, ch = uv - pr * CHR;  // pair pr = (kh, g, i)
-      const int p0 = 32 * (pr >> 4) + ((pr >> 2) & 3) + 8 * (pr & 3);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int32_t pos = x.t0 + p0 + 4 * h;
-        const int32_t bi = pos / BS - b0;
-        vid[e][h] = uv < T / 2 * CHR && pos < te ? pick(ids, bi) : -1;
-        const uint32_t off = (uint32_t)(pos % BS) * (uint32_t)a.v_seg_bytes + ch * 16;
-        vr[e][h] = *(const uint4*)(sel(vb, bi) + off);
-      }
-    }
-    if constexpr (!KQ8) {
-#pragma unroll
-      for (int e = 0; e < NCH; ++e) {
-        const int cc = t + 256 * e;
-        const int p = cc / CHR, ch = cc - p * CHR;
-        const int32_t pos = x.t0 + p;
-        const int32_t bi = pos / BS - b0;
-        kid[e] = cc < T * CHR && pos < te ? pick(ids, bi) : -1;
-        const uint32_t off = (uint32_t)(pos % BS) * (uint32_t)a.k_seg_bytes + ch * 16;
-        kr[e] = *(const uint4*)(sel(kb, bi) + off);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < NQ8; ++e) {
-        const int uq = t + 256 * e;
-        const int p = uq / UPR, rem = uq - p * UPR;
-        const int bq = rem >> 1, h = rem & 1;
-        const int32_t pos = x.t0 + p;
-        const int32_t bi = pos / BS - b0;
-        kid[e] = uq < T * UPR && pos < te ? pick(ids, bi) : -1;
-        // bytes [lb, lb + 18) of the segment: f16 scale (used when h == 0)
-        // then 16 codes; lb is even, read as five aligned dwords
-        const int lb = 34 * bq + 16 * h;
-        const uint32_t off = (uint32_t)(pos % BS) * (uint32_t)a.k_seg_bytes + (lb & ~3);
-        const uint32_t* src = (const uint32_t*)(sel(kb, bi) + off);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) qw[e][i] = src[i];
+      for (int i = 0; i < Gm::NRW; ++i) {
+        // the last copy may be partial: its idle lanes are switched off so
+        // that nothing lands past the wave's rows
+        if (i * 64 + l < Gm::CPW) copy16_to_lds(kb, qoff[i], lds_addr(&sm.raw[sl][w * Gm::RAWW + i * 1024]));
       }
     }
   };
 
-  auto keep = [](bool ok, uint4 x) {
-    return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
-  };
-  auto stage_store = [&](int b) {
+  // after this wave's copies of a tile landed: widen its q8_0 rows into
+  // K slot kb and zero the V rows of its positions that are not visible
+  auto prepare = [&](int sl, int kb, const TileD& d) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    const uint32_t mine = (uint32_t)(d.vm >> pw0) & ((1u << PPW) - 1u);
+    if (mine != (1u << PPW) - 1u) {
 #pragma unroll
-    for (int e = 0; e < NVU; ++e) {
-      const int uv = t + 256 * e;
-      if (uv < T / 2 * CHR) {
-        const int pr = uv / CHR, ch = uv - pr * CHR;
-        const int kh = pr >> 4, gg = (pr >> 2) & 3, i = pr & 3;
-        const uint4 x0 = keep(vid[e][0] >= 0, vr[e][0]);
-        const uint4 x1 = keep(vid[e][1] >= 0, vr[e][1]);
-        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // columns 8 ch + 2 k and 8 ch + 2 k + 1: low halves, then high halves
-          const int d = 8 * ch + 2 * k;
-          const int dp = d + (d >> 3);
-          sm.v[b][kh][gg][dp][i] = __builtin_amdgcn_perm(a1[k], a0[k], 0x05040100u);
-          sm.v[b][kh][gg][dp + 1][i] = __builtin_amdgcn_perm(a1[k], a0[k], 0x07060302u);
-        }
-        if (ch == 0) {
-          const int p0 = 32 * kh + gg + 8 * i;
-          sm.id[b][p0] = vid[e][0];
-          sm.id[b][p0 + 4] = vid[e][1];
-        }
+      for (int i = 0; i < Gm::NV; ++i) {
+        const int uu = i * 64 + l;
+        const int r = pw0 + uu / Gm::CHR;
+        if (!((d.vm >> r) & 1ull)) *(uint4*)&sm.v[sl][r * Gm::ROWB + (uu % Gm::CHR) * 16] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    if constexpr (!KQ8) {
+    if constexpr (KQ8) {
 #pragma unroll
-      for (int e = 0; e < NCH; ++e) {
-        const int cc = t + 256 * e;
-        if (cc < T * CHR) {
-          const int p = cc / CHR, ch = cc - p * CHR;
-          *(uint4*)&sm.k[b][p][ch * 8] = keep(kid[e] >= 0, kr[e]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < NQ8; ++e) {
-        const int uq = t + 256 * e;
-        if (uq < T * UPR) {
-          const int p = uq / UPR, rem = uq - p * UPR;
+      for (int e = 0; e < Gm::NQ8; ++e) {
+        const int uq = e * 64 + l;
+        if (uq < PPW * Gm::UPR) {
+          const int p = uq / Gm::UPR, rem = uq - p * Gm::UPR;
           const int bq = rem >> 1, h = rem & 1;
-          const int sh = (34 * bq + 16 * h) & 3;  // 0 or 2
-          const bool ok = kid[e] >= 0;
+          const int r = pw0 + p;
+          const bool ok = (d.vm >> r) & 1ull;
+          // bytes [lb, lb + 18) of the segment: f16 scale (used when h == 0)
+          // then 16 codes; lb is even, read as five aligned dwords
+          const int lb = 34 * bq + 16 * h;
+          const uint32_t* src = (const uint32_t*)&sm.raw[sl][w * Gm::RAWW + p * Gm::SEG8 + (lb & ~3)];
+          uint32_t qw[5];
+#pragma unroll
+          for (int i = 0; i < 5; ++i) qw[i] = src[i];
+          const int sh = lb & 3;  // 0 or 2
           uint32_t cw[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            cw[i] = sh ? qw[e][i + 1] : __builtin_amdgcn_alignbyte(qw[e][i + 1], qw[e][i], 2);
+            cw[i] = sh ? qw[i + 1] : __builtin_amdgcn_alignbyte(qw[i + 1], qw[i], 2);
             cw[i] = ok ? cw[i] : 0u;
           }
-          half2_t hv[8];
+          // the block scale sits in the bytes of the h == 0 unit, which is
+          // the even lane of each lane pair: take it from there
+          const uint32_t sw = ok ? (sh ? (qw[0] >> 16) : (qw[0] & 0xFFFFu)) : 0u;
+          const uint32_t sw0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sw, 0xA0, 0xF, 0xF, false);
+          const float sc8 = (float)__builtin_bit_cast(_Float16, (unsigned short)sw0);
+          // x = scale * code exactly: with u = code + 128 (sign bit flipped),
+          // x = u * scale - 128 * scale, both products exact, one rounding
+          // of an exactly representable sum
+          const float nb = -128.f * sc8;
+          half8_t hi8[2], lo8[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) codes_to_f16(cw[i], hv[2 * i], hv[2 * i + 1]);
-          half8_t lo8 = {hv[0][0], hv[0][1], hv[1][0], hv[1][1], hv[2][0], hv[2][1], hv[3][0], hv[3][1]};
-          half8_t hi8 = {hv[4][0], hv[4][1], hv[5][0], hv[5][1], hv[6][0], hv[6][1], hv[7][0], hv[7][1]};
-          *(half8_t*)&sm.k[b][p][32 * bq + 16 * h] = lo8;
-          *(half8_t*)&sm.k[b][p][32 * bq + 16 * h + 8] = hi8;
-          if (h == 0) {
-            const uint32_t sw = ok ? (sh ? (qw[e][0] >> 16) : (qw[e][0] & 0xFFFFu)) : 0u;
-            const int pidx = (p >> 4) * 16 + (p & 3) * 4 + ((p >> 2) & 3);
-            sm.ks[b][bq][pidx] = (float)__builtin_bit_cast(_Float16, (unsigned short)sw);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t y = cw[i] ^ 0x80808080u;
+            const float x0 = fmaf((float)(y & 0xFFu), sc8, nb);
+            const float x1 = fmaf((float)((y >> 8) & 0xFFu), sc8, nb);
+            const float x2 = fmaf((float)((y >> 16) & 0xFFu), sc8, nb);
+            const float x3 = fmaf((float)(y >> 24), sc8, nb);
+            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
+            hi8[i >> 1][4 * (i & 1) + 0] = h0;
+            hi8[i >> 1][4 * (i & 1) + 1] = h1;
+            hi8[i >> 1][4 * (i & 1) + 2] = h2;
+            hi8[i >> 1][4 * (i & 1) + 3] = h3;
+            lo8[i >> 1][4 * (i & 1) + 0] = (_Float16)(x0 - (float)h0);
+            lo8[i >> 1][4 * (i & 1) + 1] = (_Float16)(x1 - (float)h1);
+            lo8[i >> 1][4 * (i & 1) + 2] = (_Float16)(x2 - (float)h2);
+            lo8[i >> 1][4 * (i & 1) + 3] = (_Float16)(x3 - (float)h3);
+          }
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int off = swz<HD>(r, 4 * bq + 2 * h + e2);
+            *(half8_t*)&sm.k[kb][0][off] = hi8[e2];
+            *(half8_t*)&sm.k[kb][1][off] = lo8[e2];
           }
         }
       }
     }
   };
 
-  auto compute = [&](int b, const Walk& x) {
-    // validity of the tile's positions (wave-uniform bit mask)
-    const uint64_t vm = __builtin_amdgcn_ballot_w64(sm.id[b][l % T] >= 0);
-    const uint64_t all = T == 64 ? ~0ull : 0xffffffffull;
-    const bool full = (vm & all) == all && x.t0 + T <= lim_min_w;
-
-    // S^T = K Q^T: for 16-position tile st the lane holds positions
-    // 16 st + g + 4 i (i = 0..3) of row n16; sc[rt][4 st + i]
-    float sc[kRowTiles][NJ];
+  // S^T = K Q^T for the 32-position half kh of a tile: for 16-position tile
+  // st the lane holds positions 16 st + 4 g + i of the half, for row n16, as
+  // sc[rt][4 st + i]
+  auto scores = [&](const unsigned char* kt, int kh, float (&sc)[RT][8]) {
 #pragma unroll
-    for (int st = 0; st < T / 16; ++st) {
-      const int krow = 16 * st + (n16 >> 2) + 4 * (n16 & 3);
-      float4_t acc[kRowTiles];
+    for (int st = 0; st < 2; ++st) {
+      const int krow = 32 * kh + 16 * st + n16;
+      float4_t acc[RT];
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) acc[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const half8_t af = *(const half8_t*)&sm.k[b][krow][ks * 32 + g * 8];
-        if constexpr (!KQ8) {
+        const int off = swz<HD>(krow, 4 * ks + g);
+        const half8_t af = *(const half8_t*)&kt[off];
 #pragma unroll
-          for (int rt = 0; rt < kRowTiles; ++rt) acc[rt] = mfma16x16x32(af, qf[rt][ks], acc[rt]);
-        } else {
-          const float4_t scl = *(const float4_t*)&sm.ks[b][ks][st * 16 + g * 4];
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma16x16x32(af, qf[rt][ks], acc[rt]);
+        if constexpr (KQ8) {
+          const half8_t al = *(const half8_t*)&kt[Gm::TILEB + off];  // the lo tile follows the hi tile
 #pragma unroll
-          for (int rt = 0; rt < kRowTiles; ++rt) {
-            const float4_t part = mfma16x16x32(af, qf[rt][ks], float4_t{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rt][i] = fmaf(part[i], scl[i], acc[rt][i]);
-          }
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma16x16x32(al, qf[rt][ks], acc[rt]);
         }
       }
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[rt][4 * st + i] = acc[rt][i];
-      __builtin_amdgcn_sched_barrier(0);  // bounds the fragments in flight (register pressure)
     }
+  };
 
-    // ---- online softmax per row (the four lane groups hold the same row).
-    // The running max moves lazily: only when a row's max would grow by more
-    // than 2^8, so p stays <= 256 (exact enough in f16) and the output is
-    // rarely rescaled.  Hidden positions score -inf and so get p = 0.
-    half8_t pf[kRowTiles][NKH];
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      if (!full) {
-        // score jj is position p = 16 (jj / 4) + g + 4 (jj % 4) of the tile
-        const uint32_t vg = (uint32_t)(vm >> g);
-        const int32_t lr = lim[rt] - x.t0 - g;
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int pc = 16 * (jj >> 2) + 4 * (jj & 3);
-          const bool ok = ((vg >> pc) & 1u) && pc < lr;
-          sc[rt][jj] = ok ? sc[rt][jj] : -INFINITY;
-        }
-      }
-      float mx = sc[rt][0];
-#pragma unroll
-      for (int jj = 1; jj < NJ; ++jj) mx = fmaxf(mx, sc[rt][jj]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mc = mx * mul;
-      const bool grow = mc > m[rt] + kLazyMax;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float mn = grow ? mc : m[rt];
-        const float alpha = fast_exp2(m[rt] - mn);
-        lsum[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
-        m[rt] = mn;
-      }
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        const float p = fast_exp2(fmaf(sc[rt][jj], mul, -m[rt]));
-        lsum[rt] += p;
-        pf[rt][jj >> 3][jj & 7] = (_Float16)p;
-      }
-    }
-
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V^T P^T over each 32-position half: A gathers column d of V
-    // at positions 32 kh + g + 4 j
+  // One tile, in 32-position halves: the online softmax is exact in any
+  // order, so each half updates the running max/sum and the output in turn.
+  // The scores of the next half are issued (matrix cores) before the
+  // softmax of the current half (vector ALU), so the two overlap.
+  auto compute = [&](int sl, int kb, const TileD& d) {
+    const unsigned char* kt = KQ8 ? sm.k[kb][0] : sm.k[sl][0];
+    const unsigned char* vt = sm.v[sl];
+    const half8_t ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                          (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+    float sc[RT][8], sn[RT][8];
+    scores(kt, 0, sn);
 #pragma unroll
     for (int kh = 0; kh < NKH; ++kh) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 16 + n16;
-        const half8_t vf = *(const half8_t*)&sm.v[b][kh][g][d + (d >> 3)][0];
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) o[rt][dt] = mfma16x16x32(vf, pf[rt][kh], o[rt][dt]);
+        for (int jj = 0; jj < 8; ++jj) sc[rt][jj] = sn[rt][jj];
+      if (kh + 1 < NKH) scores(kt, kh + 1, sn);
+      const uint32_t vmh = (uint32_t)(d.vm >> (32 * kh));
+      const int32_t t0h = d.t0 + 32 * kh;
+      const bool full = vmh == 0xffffffffu && t0h + 32 <= lim_min_w;
+
+      // ---- online softmax per row (the four lane groups hold the same row).
+      // The running max moves lazily: only when a row's max would grow by
+      // more than 2^8, so p stays <= 256 (exact enough in f16) and the output
+      // is rarely rescaled.  Hidden positions score -inf and so get p = 0.
+      half8_t pf[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (!full) {
+          // score jj is position p = 16 (jj / 4) + 4 g + jj % 4 of the half
+          const uint32_t vg = vmh >> (4 * g);
+          const int32_t lr = lim[rt] - t0h - 4 * g;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int pc = 16 * (jj >> 2) + (jj & 3);
+            const bool ok = ((vg >> pc) & 1u) && pc < lr;
+            sc[rt][jj] = ok ? sc[rt][jj] : -INFINITY;
+          }
+        }
+        float mx = sc[rt][0];
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[rt][jj]);
+        mx = max_over_groups(mx);
+        const float mc = mx * mul;
+        const bool grow = mc > m[rt] + kLazyMax;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float mn = grow ? mc : m[rt];
+          const float alpha = fast_exp2(m[rt] - mn);
+#pragma unroll
+          for (int dt = 0; dt <= DT; ++dt) o[rt][dt] *= alpha;
+          m[rt] = mn;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pf[rt][jj] = (_Float16)fast_exp2(fmaf(sc[rt][jj], mul, -m[rt]));
       }
+
+      // ---- O^T += V^T P^T: two transposing reads give lane (g, n16) column
+      // dt*16 + n16 of V at positions 16 h + 4 g + e of the half (operand
+      // element 4 h + e); lane n16 addresses row 16 h + 4 g + n16 / 4 of the
+      // half at columns dt*16 + 4 (n16 % 4) ...
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        half8_t vf;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int R = 32 * kh + 16 * h + 4 * g + (n16 >> 2);
+          const int cb = 32 * dt + 8 * (n16 & 3);  // byte offset of the 4 columns in the row
+          const int off = swz<HD>(R, cb >> 4) + (cb & 15);
+          const short4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)&vt[off]);
+          const half2_t* hx = (const half2_t*)&x;
+          vf[4 * h + 0] = hx[0][0];
+          vf[4 * h + 1] = hx[0][1];
+          vf[4 * h + 2] = hx[1][0];
+          vf[4 * h + 3] = hx[1][1];
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma16x16x32(vf, pf[rt], o[rt][dt]);
+      }
+      // row sums of the rounded probabilities (every element of o[rt][DT])
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) o[rt][DT] = mfma16x16x32(ones, pf[rt], o[rt][DT]);
     }
   };
 
-  // ---- pipeline over the chunk's tiles
-  Walk wc{0, 0, 0, 0, 0, 0};
-  if (va < vend) walk_seek(a, s, lim_max, va, vend, wc);
-  else wc.r = a.n_runs;
-  if (wc.r < a.n_runs) {
-    int32_t ids[NID], idn[NID];
-    load_ids(wc, ids);
-    check_ids(wc, ids);
-    stage_issue(wc, ids);
-    stage_store(0);
-    Walk wn = wc;
-    walk_next<T>(a, s, lim_max, va, vend, wn);
-    if (wn.r < a.n_runs) load_ids(wn, idn);
+  // ---- pipeline: tile k is computed while tile k+1 is being prepared and
+  // tile k+2 copied; one barrier per tile
+  Walk wa;
+  wx.start(wa, ta, tb);
+  if (wa.r < a.n_runs) {
+    int32_t ids[NID];
+    load_ids(wa, ids);
+    TileD tc = make_tile(wa, ids);
+    issue(0, ids);
+    Walk wb = wa;
+    wx.next(wb);
+    const bool hb = wb.r < a.n_runs;
+    TileD t1{0, 0ull};
+    if (hb) {
+      load_ids(wb, ids);
+      t1 = make_tile(wb, ids);
+      issue(1, ids);
+    }
+    Walk wc = wb;
+    if (hb) wx.next(wc);
+    bool hc = hb && wc.r < a.n_runs;
+    int32_t idc[NID];
+    if (hc) load_ids(wc, idc);
+    if (hb) wait_vm<NDMA>();
+    else wait_vm<0>();
+    prepare(0, 0, tc);
     __syncthreads();
-    int b = 0;
+    bool h1 = hb;
+    int sl = 0, kb = 0;
     for (;;) {
-      const bool more = wn.r < a.n_runs;
-      Walk wnn = wn;
-      walk_next<T>(a, s, lim_max, va, vend, wnn);
-      int32_t idnn[NID];
-      if (wnn.r < a.n_runs) load_ids(wnn, idnn);
-      if (more) {
-        check_ids(wn, idn);
-        stage_issue(wn, idn);
+      // copies of tile k+2
+      TileD t2{0, 0ull};
+      if (hc) {
+        t2 = make_tile(wc, idc);
+        issue(sl == 0 ? 2 : sl - 1, idc);
       }
-      compute(b, wc);
-      if (more) stage_store(b ^ 1);
+      compute(sl, kb, tc);
+      // table entries of tile k+3: scalar loads share the LDS counter, so they
+      // are issued only after the compute's LDS reads (which would otherwise
+      // all have to wait for them)
+      Walk wd = wc;
+      if (hc) wx.next(wd);
+      const bool hd = hc && wd.r < a.n_runs;
+      int32_t idd[NID];
+      if (hd) load_ids(wd, idd);
+      // prepare tile k+1 once this wave's copies of it have landed
+      if (h1) {
+        if (hc) wait_vm<NDMA>();
+        else wait_vm<0>();
+        prepare(sl == 2 ? 0 : sl + 1, kb ^ 1, t1);
+      }
       __syncthreads();
-      if (!more) break;
-      wc = wn;
-      wn = wnn;
+      if (!h1) break;
+      tc = t1;
+      t1 = t2;
+      h1 = hc;
+      wc = wd;
+      hc = hd;
 #pragma unroll
-      for (int i = 0; i < NID; ++i) idn[i] = idnn[i];
-      b ^= 1;
+      for (int i = 0; i < NID; ++i) idc[i] = idd[i];
+      sl = sl == 2 ? 0 : sl + 1;
+      kb ^= 1;
     }
   }
+  if (bad && (a.flags & PKV_FLAG_CHECKED) && a.err && kvh == 0 && qb == 0 && t == 0) atomicAdd(a.err, bad);
 
   // ---- finish: sum the row's lane groups; write the output or the partial
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    float ls = lsum[rt];
-    ls += shfl_xor(ls, 16);
-    ls += shfl_xor(ls, 32);
+  for (int rt = 0; rt < RT; ++rt) {
+    const float ls = o[rt][DT][0];
     if (!rok[rt]) continue;
     const bool empty = m[rt] == kEmptyMax;
     const int64_t row = (int64_t)jq[rt] * a.n_q_heads + kvh * G + hq[rt];
@@ -621,13 +756,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a) {
 
 namespace {
 
-constexpr int tile_for(int hd) { return hd <= 128 ? 32 : 32; }
-
 // Chunks per window: enough workgroups to fill the chip twice over, each
 // chunk still at least four tiles of the largest possible window.
 int plan_chunks(const AttnArgs& a, int hd, int g) {
-  const int T = tile_for(hd);
-  const int qpb = kRowsWG / g;
+  const int T = tile_of(hd);
+  const int qpb = rows_per_wg(hd) / g;
   const int64_t nqb = ((int64_t)a.max_q + qpb - 1) / qpb;
   const int64_t base = (int64_t)a.n_seqs * a.n_kv_heads * (nqb > 0 ? nqb : 1);
   int64_t nch = (kTargetTasks + base - 1) / base;
@@ -669,21 +802,20 @@ hipError_t launch_prefill(const AttnArgs& a0, int combo, int hd, int bs, int g, 
     a.part_ml = (float*)base;
     a.part_o = (float*)(base + align256(rows * 2 * sizeof(float)));
   }
-  const int qpb = kRowsWG / g;
+  const int qpb = rows_per_wg(hd) / g;
   const int32_t nqb = (a.max_q + qpb - 1) / qpb;
   const int64_t n_tasks = (int64_t)a.n_seqs * a.n_kv_heads * a.nch * nqb;
   if (n_tasks > (int64_t)1 << 28) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n_tasks + 7) / 8 * 8));
-#define PKV_PCASE(HD, BS, G)                                                                          \
-  if (hd == HD && bs == BS && g == G) {                                                               \
-    constexpr int T = tile_for(HD);                                                                   \
-    if (q8)                                                                                           \
-      hipLaunchKernelGGL((prefill_kernel<HD, BS, G, true, T>), grid, dim3(256), 0, st, a,             \
-                         (int32_t)n_tasks, nqb);                                                      \
-    else                                                                                              \
-      hipLaunchKernelGGL((prefill_kernel<HD, BS, G, false, T>), grid, dim3(256), 0, st, a,            \
-                         (int32_t)n_tasks, nqb);                                                      \
-    *found = true;                                                                                    \
+#define PKV_PCASE(HD, BS, G)                                                                      \
+  if (hd == HD && bs == BS && g == G) {                                                           \
+    if (q8)                                                                                       \
+      hipLaunchKernelGGL((prefill_kernel<HD, BS, G, true>), grid, dim3(512), 0, st, a, a.table,   \
+                         a.window, a.k_pool, a.v_pool, (int32_t)n_tasks, nqb);                    \
+    else                                                                                          \
+      hipLaunchKernelGGL((prefill_kernel<HD, BS, G, false>), grid, dim3(512), 0, st, a, a.table,  \
+                         a.window, a.k_pool, a.v_pool, (int32_t)n_tasks, nqb);                    \
+    *found = true;                                                                                \
   }
 #define PKV_PCASES_G(HD, BS) PKV_PCASE(HD, BS, 1) PKV_PCASE(HD, BS, 2) PKV_PCASE(HD, BS, 3) PKV_PCASE(HD, BS, 4) PKV_PCASE(HD, BS, 8)
   PKV_PCASES_G(64, 16)
