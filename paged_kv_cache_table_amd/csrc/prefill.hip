@@ -16,8 +16,10 @@
 // runs' tiles in order form one list that is cut into nch equal chunks.  With
 // nch > 1 each workgroup writes (max, sum, unnormalised output) per row and a
 // merge kernel combines them with the log-sum-exp rule; with nch = 1 the
-// output is written directly.  Workgroups that share a chunk's K/V are
-// numbered so that they land on the same XCD.
+// output is written directly.  A one-workgroup kernel first orders the
+// sequences by their number of window tiles; workgroups are numbered longest
+// sequence first, so that the longest chunks start first and shorter ones
+// fill the machine behind them.
 //
 // Data movement.  A tile is T/BS whole blocks.  Each wave copies its T/8
 // positions of a tile (which lie in one block: one scalar base address per
@@ -59,7 +61,19 @@ constexpr int kRing = 3;            // LDS tile slots: copies run two tiles ahea
 constexpr float kEmptyMax = -1e30f;
 constexpr float kLazyMax = 8.0f;    // log2 growth of a row max that forces a rescale
 constexpr int kTargetTasks = 512;   // workgroups the chunking aims for
-constexpr int kMaxChunks = 16;
+constexpr int kMaxChunks = 16;      // unless a chunk would exceed kMaxTiles
+constexpr int kMaxTiles = 256;      // tiles of one workgroup's chunk (its list lives in LDS)
+
+// One tile of a workgroup's chunk, described once before the main loop: its
+// first position (a multiple of the tile size), the visibility mask of its
+// positions (inside the run, not in a hole) and its checked block ids
+// (-1: hole or out of range).
+struct __attribute__((aligned(16))) TileRec {
+  int32_t t0;
+  uint32_t vm_lo, vm_hi;
+  int32_t pad;
+  int32_t blk[4];
+};
 
 // Tile shape per head_dim: positions per tile and 16-row tiles per wave.
 __host__ __device__ constexpr int tile_of(int hd) { return hd <= 128 ? 64 : 32; }
@@ -94,6 +108,7 @@ struct __attribute__((aligned(16))) PrefillSmem {
   // tiles with hi + lo == scale * code exactly
   unsigned char k[KQ8 ? 2 : kRing][KQ8 ? 2 : 1][Gm::TILEB];
   unsigned char raw[KQ8 ? kRing : 1][KQ8 ? kPWaves * Gm::RAWW : 16];  // q8_0 tiles as stored
+  TileRec tiles[kMaxTiles];                                           // this workgroup's chunk
   int32_t lim_max;                                                    // largest causal limit of the rows
 };
 
@@ -120,14 +135,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 // 16 bytes from base + off (base wave-uniform, off per lane) to lds + 16 * lane.
-// base and lds are read through readfirstlane so that they are scalar
-// registers whatever the compiler can prove about their uniformity.
+// Callers derive base and lds from readfirstlane results only, so both are
+// scalar registers.
 __device__ __forceinline__ void copy16_to_lds(const unsigned char* base, uint32_t off, uint32_t lds) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint64_t bu = ((uint64_t)(uint32_t)uni((int32_t)(b >> 32)) << 32) | (uint32_t)uni((int32_t)(uint32_t)b);
-  const uint32_t lu = (uint32_t)uni((int32_t)lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
-               "s"((const unsigned char*)(uintptr_t)bu), "s"(lu)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 
@@ -189,17 +200,9 @@ __device__ inline void run_bounds(const AttnArgs& a, const int32_t* __restrict__
   hi = uni((int32_t)x1);
 }
 
-// This workgroup's walk over the window.  Each run, clipped to [0, lim), is
-// covered by the T-aligned tiles that meet it (its first and last tile may be
-// partial); the runs' tiles in order form one list of which the workgroup
-// takes [ta, tb).  All fields are wave-uniform.
-struct Walk {
-  int32_t r;       // current run (== n_runs: finished)
-  int32_t lo, hi;  // run r clipped
-  int32_t k, n;    // tile k of the run's n tiles
-  int32_t left;    // tiles left in the chunk
-};
-
+// The runs of a sequence's window, clipped to [0, lim), each covered by the
+// T-aligned tiles that meet it (its first and last tile may be partial); the
+// runs' tiles in order form one list that is cut into the chunks.
 template <int T>
 struct WalkCtx {
   const AttnArgs& a;
@@ -211,40 +214,6 @@ struct WalkCtx {
     run_bounds(a, window, s, r, lim, lo, hi);
     return hi > lo ? (hi + T - 1) / T - lo / T : 0;
   }
-  // position the walk on tile ta of the list, ending at tb
-  __device__ void start(Walk& w, int32_t ta, int32_t tb) const {
-    w.left = tb - ta;
-    w.r = a.n_runs;
-    if (w.left <= 0) return;
-    int32_t before = 0;
-    for (int r = 0; r < a.n_runs; ++r) {
-      int32_t lo, hi;
-      const int32_t n = tiles(r, lo, hi);
-      if (ta < before + n) {
-        w.r = r;
-        w.lo = lo;
-        w.hi = hi;
-        w.n = n;
-        w.k = ta - before;
-        return;
-      }
-      before += n;
-    }
-  }
-  __device__ void next(Walk& w) const {
-    if (w.r >= a.n_runs) return;
-    if (--w.left <= 0) {
-      w.r = a.n_runs;
-      return;
-    }
-    if (++w.k < w.n) return;
-    do {
-      ++w.r;
-      w.k = 0;
-      w.n = w.r < a.n_runs ? tiles(w.r, w.lo, w.hi) : 0;
-    } while (w.r < a.n_runs && w.n == 0);
-  }
-  __device__ int32_t t0(const Walk& w) const { return (w.lo / T + w.k) * T; }
 };
 
 // One staged tile (wave-uniform): it starts at t0 (a multiple of T) and vm
@@ -259,7 +228,7 @@ template <int HD, int BS, int G, bool KQ8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t* __restrict__ window,
                     const unsigned char* __restrict__ kpool, const unsigned char* __restrict__ vpool,
-                    int32_t n_tasks, int32_t nqb) {
+                    const int32_t* __restrict__ order, int32_t n_tasks, int32_t nqb) {
   using Gm = PGeom<HD>;
   constexpr int T = Gm::T;
   constexpr int RT = Gm::RT;
@@ -273,16 +242,19 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   static_assert(BS == 16 || BS == 32, "a tile is whole blocks and a wave's positions one block");
   __shared__ PrefillSmem<HD, KQ8> sm;
 
-  // ---- task: ((s * Hkv + kvh) * nch + c) * nqb + qb, XCD-major numbering
-  const int32_t n8 = (n_tasks + 7) >> 3;
-  const int32_t u = (int32_t)(blockIdx.x & 7) * n8 + (int32_t)(blockIdx.x >> 3);
+  // ---- task u = ((rank * nch + c) * Hkv + kvh) * nqb + qb: the sequences in
+  // order of decreasing window size (longest first), so that the longest
+  // chunks start first and the short ones fill in behind them
+  const int32_t u = (int32_t)blockIdx.x;
   if (u >= n_tasks) return;
   const int qb = u % nqb;
   int32_t rest = u / nqb;
-  const int c = rest % a.nch;
-  rest /= a.nch;
   const int kvh = rest % a.n_kv_heads;
-  const int s = rest / a.n_kv_heads;
+  rest /= a.n_kv_heads;
+  const int c = rest % a.nch;
+  const int32_t rank = rest / a.nch;
+  int s = order[rank];
+  s = s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
 
   const int t = threadIdx.x, w = uni(t >> 6), l = t & 63, g = l >> 4, n16 = l & 15;
   int q0 = a.cu_q[s], q1 = a.cu_q[s + 1];
@@ -344,7 +316,49 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     NT += wx.tiles(r, lo, hi);
   }
   const int32_t per = (NT + a.nch - 1) / a.nch;
-  const int32_t ta = c * per, tb = ta + per < NT ? ta + per : NT;
+  const int32_t ta = c * per;
+  int32_t ntl = (ta + per < NT ? ta + per : NT) - ta;  // tiles in this chunk
+  if (ntl > kMaxTiles) ntl = kMaxTiles;                // the host sizes chunks below this
+  if (ntl < 0) ntl = 0;
+
+  const unsigned char* kbase = kpool + (int64_t)kvh * BS * a.k_seg_bytes;
+  const unsigned char* vbase = vpool + (int64_t)kvh * BS * a.v_seg_bytes;
+  const int32_t* trow = table + (int64_t)s * a.max_blocks;
+  int32_t bad = 0;  // out-of-range table entries seen (checked mode)
+
+  // thread i describes tile ta + i of the list
+  for (int i = t; i < ntl; i += 64 * kPWaves) {
+    int32_t idx = ta + i, lo = 0, hi = 0;
+    for (int r = 0; r < a.n_runs; ++r) {
+      const int32_t n = wx.tiles(r, lo, hi);
+      if (idx < n) break;
+      idx -= n;
+    }
+    TileRec rc;
+    rc.t0 = (lo / T + idx) * T;
+    const int32_t vlo = (lo > rc.t0 ? lo : rc.t0) - rc.t0;
+    const int32_t vhi = (hi < rc.t0 + T ? hi : rc.t0 + T) - rc.t0;
+    uint64_t vm = (vhi >= 64 ? ~0ull : (1ull << vhi) - 1ull) & ~((1ull << vlo) - 1ull);
+    rc.pad = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int32_t id = -1;
+      if (j < NID) {
+        const int32_t b = rc.t0 / BS + j;
+        const int32_t raw = b < a.max_blocks ? trow[b] : -1;
+        const bool ok = raw >= 0 && raw < a.n_pool_blocks;
+        const uint64_t bm = ((1ull << BS) - 1ull) << (j * BS);
+        if (!ok && raw != -1 && (vm & bm)) ++bad;
+        if (!ok) vm &= ~bm;
+        id = ok ? raw : -1;
+      }
+      rc.blk[j] = id;
+    }
+    rc.vm_lo = (uint32_t)vm;
+    rc.vm_hi = (uint32_t)(vm >> 32);
+    sm.tiles[i] = rc;
+  }
+  __syncthreads();
 
   float m[RT];
   float4_t o[RT][DT + 1];  // o[rt][DT]: the row's sum of probabilities
@@ -355,15 +369,11 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     for (int dt = 0; dt <= DT; ++dt) o[rt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const unsigned char* kbase = kpool + (int64_t)kvh * BS * a.k_seg_bytes;
-  const unsigned char* vbase = vpool + (int64_t)kvh * BS * a.v_seg_bytes;
-  const int32_t* trow = table + (int64_t)s * a.max_blocks;
   // |scale| * log2(e), kept above 0 so that a hidden score (-inf) always
   // gives p = 0 (a zero scale then weighs every visible position equally)
   const float mul = fmaxf(fabsf(a.score_mul), 1e-30f);
   const int pw0 = w * PPW;    // first position this wave copies and prepares
   const int wblk = pw0 / BS;  // the tile block holding this wave's positions
-  int32_t bad = 0;            // out-of-range table entries seen (checked mode)
 
   // per-lane byte offsets inside a (block, kv head) region: tile-invariant
   uint32_t voff[Gm::NV], qoff[KQ8 ? Gm::NRW : 1];
@@ -378,49 +388,38 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     for (int i = 0; i < Gm::NRW; ++i) qoff[i] = (uint32_t)((pw0 & (BS - 1)) * Gm::SEG8 + (i * 64 + l) * 16);
   }
 
-  // block ids of a tile (raw table entries; -1 past the table)
-  auto load_ids = [&](const Walk& x, int32_t (&ids)[NID]) {
-    const int32_t b0 = wx.t0(x) / BS;
-#pragma unroll
-    for (int i = 0; i < NID; ++i) ids[i] = b0 + i < a.max_blocks ? trow[b0 + i] : -1;
-  };
-  // tile descriptor; ids become checked block ids (-1: hole or out of range)
-  auto make_tile = [&](const Walk& x, int32_t (&ids)[NID]) {
+  // tile k of the list as the compute needs it (wave-uniform)
+  auto tile_at = [&](int k) {
+    const TileRec& rc = sm.tiles[k];
     TileD d;
-    d.t0 = wx.t0(x);
-    const int32_t lo = (x.lo > d.t0 ? x.lo : d.t0) - d.t0;
-    const int32_t hi = (x.hi < d.t0 + T ? x.hi : d.t0 + T) - d.t0;
-    uint64_t vm = (hi >= 64 ? ~0ull : (1ull << hi) - 1ull) & ~((1ull << lo) - 1ull);
-#pragma unroll
-    for (int i = 0; i < NID; ++i) {
-      const int32_t id = uni(ids[i]);
-      const bool ok = id >= 0 && id < a.n_pool_blocks;
-      const uint64_t bm = ((1ull << BS) - 1ull) << (i * BS);
-      if (!ok && id != -1 && (vm & bm)) ++bad;
-      if (!ok) vm &= ~bm;
-      ids[i] = ok ? id : -1;
-    }
-    d.vm = vm;
+    d.t0 = uni(rc.t0);
+    d.vm = ((uint64_t)(uint32_t)uni((int32_t)rc.vm_hi) << 32) | (uint32_t)uni((int32_t)rc.vm_lo);
     return d;
   };
 
-  // copy this wave's positions of a tile into LDS slot sl (no waiting); a
+  // copy this wave's positions of tile k into LDS slot sl (no waiting); a
   // block that is a hole copies block 0, which always exists
-  auto issue = [&](int sl, const int32_t (&ids)[NID]) {
-    const int64_t blk = ids[wblk] >= 0 ? ids[wblk] : 0;
+  auto issue = [&](int sl, int k) {
+    const int32_t id = uni(sm.tiles[k].blk[wblk]);
+    const int64_t blk = id >= 0 ? id : 0;
     const unsigned char* vb = vbase + blk * a.v_block_bytes;
     const unsigned char* kb = kbase + blk * a.k_block_bytes;
+    const uint32_t lv = (uint32_t)uni((int32_t)lds_addr(&sm.v[sl][pw0 * Gm::ROWB]));
 #pragma unroll
     for (int i = 0; i < Gm::NV; ++i) {
-      copy16_to_lds(vb, voff[i], lds_addr(&sm.v[sl][pw0 * Gm::ROWB + i * 1024]));
-      if constexpr (!KQ8) copy16_to_lds(kb, voff[i], lds_addr(&sm.k[sl][0][pw0 * Gm::ROWB + i * 1024]));
+      copy16_to_lds(vb, voff[i], lv + i * 1024);
+      if constexpr (!KQ8) {
+        const uint32_t lk = (uint32_t)uni((int32_t)lds_addr(&sm.k[sl][0][pw0 * Gm::ROWB]));
+        copy16_to_lds(kb, voff[i], lk + i * 1024);
+      }
     }
     if constexpr (KQ8) {
+      const uint32_t lr = (uint32_t)uni((int32_t)lds_addr(&sm.raw[sl][w * Gm::RAWW]));
 #pragma unroll
       for (int i = 0; i < Gm::NRW; ++i) {
         // the last copy may be partial: its idle lanes are switched off so
         // that nothing lands past the wave's rows
-        if (i * 64 + l < Gm::CPW) copy16_to_lds(kb, qoff[i], lds_addr(&sm.raw[sl][w * Gm::RAWW + i * 1024]));
+        if (i * 64 + l < Gm::CPW) copy16_to_lds(kb, qoff[i], lr + i * 1024);
       }
     }
   };
@@ -616,66 +615,27 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
 
   // ---- pipeline: tile k is computed while tile k+1 is being prepared and
   // tile k+2 copied; one barrier per tile
-  Walk wa;
-  wx.start(wa, ta, tb);
-  if (wa.r < a.n_runs) {
-    int32_t ids[NID];
-    load_ids(wa, ids);
-    TileD tc = make_tile(wa, ids);
-    issue(0, ids);
-    Walk wb = wa;
-    wx.next(wb);
-    const bool hb = wb.r < a.n_runs;
-    TileD t1{0, 0ull};
-    if (hb) {
-      load_ids(wb, ids);
-      t1 = make_tile(wb, ids);
-      issue(1, ids);
-    }
-    Walk wc = wb;
-    if (hb) wx.next(wc);
-    bool hc = hb && wc.r < a.n_runs;
-    int32_t idc[NID];
-    if (hc) load_ids(wc, idc);
-    if (hb) wait_vm<NDMA>();
+  if (ntl > 0) {
+    issue(0, 0);
+    if (ntl > 1) issue(1, 1);
+    if (ntl > 1) wait_vm<NDMA>();
     else wait_vm<0>();
-    prepare(0, 0, tc);
+    prepare(0, 0, tile_at(0));
     __syncthreads();
-    bool h1 = hb;
-    int sl = 0, kb = 0;
-    for (;;) {
-      // copies of tile k+2
-      TileD t2{0, 0ull};
-      if (hc) {
-        t2 = make_tile(wc, idc);
-        issue(sl == 0 ? 2 : sl - 1, idc);
-      }
-      compute(sl, kb, tc);
-      // table entries of tile k+3: scalar loads share the LDS counter, so they
-      // are issued only after the compute's LDS reads (which would otherwise
-      // all have to wait for them)
-      Walk wd = wc;
-      if (hc) wx.next(wd);
-      const bool hd = hc && wd.r < a.n_runs;
-      int32_t idd[NID];
-      if (hd) load_ids(wd, idd);
+    int sl = 0;
+    for (int k = 0;; ++k) {
+      const int sl1 = sl == 2 ? 0 : sl + 1, sl2 = sl1 == 2 ? 0 : sl1 + 1;
+      if (k + 2 < ntl) issue(sl2, k + 2);
+      compute(sl, k & 1, tile_at(k));
       // prepare tile k+1 once this wave's copies of it have landed
-      if (h1) {
-        if (hc) wait_vm<NDMA>();
+      if (k + 1 < ntl) {
+        if (k + 2 < ntl) wait_vm<NDMA>();
         else wait_vm<0>();
-        prepare(sl == 2 ? 0 : sl + 1, kb ^ 1, t1);
+        prepare(sl1, (k + 1) & 1, tile_at(k + 1));
       }
       __syncthreads();
-      if (!h1) break;
-      tc = t1;
-      t1 = t2;
-      h1 = hc;
-      wc = wd;
-      hc = hd;
-#pragma unroll
-      for (int i = 0; i < NID; ++i) idc[i] = idd[i];
-      sl = sl == 2 ? 0 : sl + 1;
-      kb ^= 1;
+      if (k + 1 >= ntl) break;
+      sl = sl1;
     }
   }
   if (bad && (a.flags & PKV_FLAG_CHECKED) && a.err && kvh == 0 && qb == 0 && t == 0) atomicAdd(a.err, bad);
@@ -707,6 +667,57 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       }
     }
   }
+}
+
+// Orders the sequences by decreasing number of window tiles (about the
+// prefill kernel's work per sequence), ties by index; one workgroup, bitonic
+// sort in LDS.  More than kOrderMax sequences keep their own order.
+constexpr int kOrderMax = 4096;
+
+template <int T, int BS>
+__global__ __launch_bounds__(1024) void prefill_order_kernel(AttnArgs a, int32_t* order) {
+  __shared__ uint64_t key[kOrderMax];
+  const int n = a.n_seqs, t = threadIdx.x;
+  if (n > kOrderMax) {
+    for (int i = t; i < n; i += 1024) order[i] = i;
+    return;
+  }
+  int np = 1;
+  while (np < n) np <<= 1;
+  for (int i = t; i < np; i += 1024) {
+    uint64_t kk = ~0ull;  // padding sorts last
+    if (i < n) {
+      // the window clipped to the sequence length (the order only needs to
+      // be roughly right, so the queries' causal limits are not consulted)
+      const int32_t L = clamp_seq_len(a.seq_lens[i], a.max_blocks, BS);
+      int32_t nt = 0;
+      for (int r = 0; r < a.n_runs; ++r) {
+        int32_t lo, hi;
+        run_range(a, i, r, L, lo, hi);
+        nt += hi > lo ? (hi + T - 1) / T - lo / T : 0;
+      }
+      kk = ((uint64_t)(uint32_t)(0x7fffffff - nt) << 32) | (uint32_t)i;
+    }
+    key[i] = kk;
+  }
+  __syncthreads();
+  for (int size = 2; size <= np; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = t; i < np; i += 1024) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const uint64_t x = key[i], y = key[j];
+          if ((x > y) == up) {
+            key[i] = y;
+            key[j] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = t; i < n; i += 1024) order[i] = (int32_t)(uint32_t)key[i];
 }
 
 // Combine the chunk partials of each (query, q head) row:
@@ -757,7 +768,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a) {
 namespace {
 
 // Chunks per window: enough workgroups to fill the chip twice over, each
-// chunk still at least four tiles of the largest possible window.
+// chunk still at least four tiles of the largest possible window, and never
+// more than kMaxTiles tiles (a run of the table's width spans at most
+// width / T + 2 tiles).
 int plan_chunks(const AttnArgs& a, int hd, int g) {
   const int T = tile_of(hd);
   const int qpb = rows_per_wg(hd) / g;
@@ -765,9 +778,13 @@ int plan_chunks(const AttnArgs& a, int hd, int g) {
   const int64_t base = (int64_t)a.n_seqs * a.n_kv_heads * (nqb > 0 ? nqb : 1);
   int64_t nch = (kTargetTasks + base - 1) / base;
   if (nch > kMaxChunks) nch = kMaxChunks;
-  const int64_t wmax = (int64_t)(a.mode == PKV_WIN_KV_MAP ? a.n_runs : 1) * a.max_blocks * a.block_size;
-  const int64_t cap = wmax / (4 * T);
+  const int64_t runs = a.mode == PKV_WIN_KV_MAP ? a.n_runs : 1;
+  const int64_t width = (int64_t)a.max_blocks * a.block_size;
+  const int64_t cap = runs * width / (4 * T);
   if (nch > cap) nch = cap;
+  const int64_t tiles_bound = runs * (width / T + 2);
+  const int64_t need = (tiles_bound + kMaxTiles - 1) / kMaxTiles;
+  if (nch < need) nch = need;
   return nch < 1 ? 1 : (int)nch;
 }
 
@@ -780,10 +797,11 @@ size_t prefill_workspace(const AttnArgs& a, int combo, int hd, int bs, int g, bo
   *found = combo == kComboF16 || combo == kComboQ8H;
   if (!*found) return 0;
   const int nch = plan_chunks(a, hd, g);
-  size_t need = 0;
+  // sequence order, then (max, sum) and output partials when nch > 1
+  size_t need = align256((size_t)a.n_seqs * sizeof(int32_t));
   if (nch > 1) {
     const size_t rows = (size_t)a.n_q_total * a.n_q_heads * nch;
-    need = align256(rows * 2 * sizeof(float)) + align256(rows * hd * sizeof(float));
+    need += align256(rows * 2 * sizeof(float)) + align256(rows * hd * sizeof(float));
   }
   if (a.flags & PKV_FLAG_CHECKED) need += 256;
   return need;
@@ -796,9 +814,11 @@ hipError_t launch_prefill(const AttnArgs& a0, int combo, int hd, int bs, int g, 
   const bool q8 = combo == kComboQ8H;
   AttnArgs a = a0;
   a.nch = plan_chunks(a, hd, g);
+  unsigned char* base = (unsigned char*)a0.part_o;
+  int32_t* order = (int32_t*)base;
+  base += align256((size_t)a.n_seqs * sizeof(int32_t));
   if (a.nch > 1) {
     const size_t rows = (size_t)a.n_q_total * a.n_q_heads * a.nch;
-    unsigned char* base = (unsigned char*)a0.part_o;
     a.part_ml = (float*)base;
     a.part_o = (float*)(base + align256(rows * 2 * sizeof(float)));
   }
@@ -806,15 +826,25 @@ hipError_t launch_prefill(const AttnArgs& a0, int combo, int hd, int bs, int g, 
   const int32_t nqb = (a.max_q + qpb - 1) / qpb;
   const int64_t n_tasks = (int64_t)a.n_seqs * a.n_kv_heads * a.nch * nqb;
   if (n_tasks > (int64_t)1 << 28) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)((n_tasks + 7) / 8 * 8));
+  const dim3 grid((unsigned)n_tasks);
+  if (bs == 16) {
+    if (hd <= 128) hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 16>), dim3(1), dim3(1024), 0, st, a, order);
+    else hipLaunchKernelGGL((prefill_order_kernel<tile_of(256), 16>), dim3(1), dim3(1024), 0, st, a, order);
+  } else {
+    hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 32>), dim3(1), dim3(1024), 0, st, a, order);
+  }
+  {
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
 #define PKV_PCASE(HD, BS, G)                                                                      \
   if (hd == HD && bs == BS && g == G) {                                                           \
     if (q8)                                                                                       \
       hipLaunchKernelGGL((prefill_kernel<HD, BS, G, true>), grid, dim3(512), 0, st, a, a.table,   \
-                         a.window, a.k_pool, a.v_pool, (int32_t)n_tasks, nqb);                    \
+                         a.window, a.k_pool, a.v_pool, order, (int32_t)n_tasks, nqb);             \
     else                                                                                          \
       hipLaunchKernelGGL((prefill_kernel<HD, BS, G, false>), grid, dim3(512), 0, st, a, a.table,  \
-                         a.window, a.k_pool, a.v_pool, (int32_t)n_tasks, nqb);                    \
+                         a.window, a.k_pool, a.v_pool, order, (int32_t)n_tasks, nqb);             \
     *found = true;                                                                                \
   }
 #define PKV_PCASES_G(HD, BS) PKV_PCASE(HD, BS, 1) PKV_PCASE(HD, BS, 2) PKV_PCASE(HD, BS, 3) PKV_PCASE(HD, BS, 4) PKV_PCASE(HD, BS, 8)
