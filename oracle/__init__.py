@@ -18,6 +18,9 @@ written from the source pages directly:
 * "KV cache" (sipllm), section "Problem": a decode step dots the new query
   against the stored history; section "Design": the dense [pos][kv_dim]
   layout used here as the contiguous reference layout.
+* "KV Cache Design", section 3: the store's q8_0 quantizer (scale amax/127
+  kept as f16, codes rounded to nearest, ties to even); the store writes a
+  token's rows through the block table.
 
 Arithmetic is float64 numpy; byte work is exact.  Readings of points the
 pages leave open are stated in the docstrings where they are used.
@@ -38,3 +41,4 @@ from .attention import (  # noqa: F401
     paged_prefill,
 )
 from .moves import order_moves, copy_cells, copy_cells_rowwise, provenance  # noqa: F401
+from .store import quantize_q8_0, encode_rows, destination_rows, store_rows  # noqa: F401
