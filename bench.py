@@ -18,7 +18,7 @@ resident in HBM.  Prints one JSON line:
   workload on this host.
 
 Other workloads (for the record; the default is the headline): decode1,
-decode2, decode5, prefill4, copy5b; and calib, a plain device copy of known
+decode2, decode5, prefill4, copy5b, store4; and calib, a plain device copy of known
 size used to scale the HBM byte counters.
 
 Counter summary (turns two rocprofv3 --pmc runs, FETCH_SIZE then WRITE_SIZE,
@@ -403,13 +403,74 @@ def run_copy(args):
     }
 
 
+def run_store(args):
+    """The store that fills the windowed-prefill pools: every position of the
+    16 sequences (93,809 tokens), f16 rows into the q8_0 K pool (store
+    quantizer) and the f16 V pool, through the block table."""
+    import torch
+
+    import paged_kv_cache_table_amd as pkv
+    from workloads import gen as wgen
+
+    w = wgen.make(4)
+    st = wgen.store_of_workload(w, src_fmt="f16")
+    log(f"[bench] store: {st.n_tok} tokens of workload 4 into its q8_0 K / f16 V pools")
+    k_new, v_new = wgen.store_values(st, "cuda")
+    kp = torch.zeros((st.n_pool_blocks, st.n_kv_heads, st.block_size, wgen.pool_width("q8_0", st.head_dim)),
+                     dtype=torch.uint8, device="cuda")
+    vp = torch.zeros((st.n_pool_blocks, st.n_kv_heads, st.block_size, st.head_dim), dtype=torch.float16,
+                     device="cuda")
+    table = torch.from_numpy(st.block_table).cuda()
+    pos = torch.from_numpy(st.pos).cuda()
+    sid = torch.from_numpy(st.seq_ids).cuda()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def call():
+        pkv.kv_store(k_new, v_new, pos, kp, vp, table, seq_ids=sid)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.mean(times))
+    n = st.n_tok
+    seg_k = wgen.q8_0_seg_bytes(st.head_dim)
+    src_bytes = 2 * n * st.n_kv_heads * st.head_dim * 2            # K and V rows read, f16
+    dst_bytes = n * st.n_kv_heads * (seg_k + 2 * st.head_dim)       # q8_0 K and f16 V rows written
+    idx_bytes = n * 8                                               # positions and sequence ids
+    total = src_bytes + dst_bytes + idx_bytes
+    gbs = total / (ms * 1e-3) / 1e9
+    return {
+        "metric": "KV store (q8_0 K quantizer + f16 V): HBM GB/s (% HBM peak) and tokens/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 -> q8_0 / f16", "data": "synthetic",
+        "config": {"workload": f"store of {n} tokens (16 seqs of 2048..8192 positions, 8 kv heads, hd 128, block 32, "
+                               "tables from a 2^13-block pool): f16 K rows -> q8_0, f16 V rows -> f16; "
+                               "cache flushed per step",
+                   "tokens": n, "bytes": total},
+        "tokens_per_s": round(n / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "store_kernel", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode3",
-                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "calib"])
+                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "calib"])
     ap.add_argument("--pmc-summary", nargs=5, metavar=("KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
     ap.add_argument("--split", type=int, default=0, help="decode split size in tokens (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -439,6 +500,8 @@ def main(argv=None):
             res["cpu_baseline"] = None
     elif args.workload == "prefill4":
         res = run_prefill(args)
+    elif args.workload == "store4":
+        res = run_store(args)
     elif args.workload == "copy5b":
         res = run_copy(args)
     else:

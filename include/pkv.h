@@ -227,6 +227,50 @@ pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, 
                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Store: write the K and V rows of n_tok new tokens into the pools through
+ * the block table, each in its pool's format — the write that precedes
+ * every read ("KV Cache Design", section 2 names the store op of the fused
+ * decode family; "Tiered KV cache — architecture", section "The
+ * paged-attention block model": position p of sequence s lives in physical
+ * block table[s][p / block_size] at slot p % block_size).
+ *
+ * Formats ("KV Cache Design", section 3: one quantizer for every store):
+ *  - q8_0: per 32 values, d = amax / 127 in binary32; each code is x / d
+ *    (binary32 division) rounded to nearest, ties to even, clamped to
+ *    [-127, 127]; the stored scale is d rounded to binary16 (nearest-even).
+ *    amax = 0 gives scale 0 and zero codes.  Codes are taken against d, so
+ *    a block whose scale underflows binary16 keeps its codes with scale 0.
+ *    Bytes past the last block of a segment (head_dim / 32 odd) are zero.
+ *  - f16: the source rounded to binary16 (nearest-even); f32: exact.
+ *  Inputs are finite, and amax / 127 fits binary16; other values are
+ *  outside the format and give unspecified bytes.
+ *
+ * shape: n_seqs, n_kv_heads, head_dim (32, 64, 128 or 256), block_size,
+ *   n_pool_blocks, max_blocks_per_seq, k_fmt and v_fmt are used; the other
+ *   fields are ignored.
+ * src_fmt: PKV_F32 or PKV_F16, the type of k_new and v_new.
+ * k_new, v_new: device [n_tok][n_kv_heads][head_dim] of src_fmt, 16-byte
+ *   aligned.  v_new and v_pool may both be NULL (store K only).
+ * seq_ids: device int32 [n_tok], the sequence of each token, or NULL: token
+ *   t belongs to sequence t (then n_tok <= n_seqs).
+ * positions: device int32 [n_tok], the position of each token.
+ * block_table: device int32 [n_seqs][max_blocks_per_seq].
+ * k_pool, v_pool: device pools as for attention, 16-byte aligned.
+ * skipped: device int32, or NULL.  A token whose sequence lies outside
+ *   [0, n_seqs), whose position lies outside [0, max_blocks_per_seq *
+ *   block_size), or whose table entry is not a block of the pool (the
+ *   sentinel included) is not stored: its rows are left as they were and 1
+ *   is added to *skipped (the caller clears it).
+ * Destinations must be distinct: a row named by two tokens of one call
+ * holds unspecified bytes.  Only the named rows are written.  n_tok = 0 is
+ * a no-op whatever the pointers are.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_kv_store(const pkv_shape* shape, int32_t n_tok, int32_t src_fmt, const void* k_new,
+                        const void* v_new, const int32_t* seq_ids, const int32_t* positions,
+                        const int32_t* block_table, void* k_pool, void* v_pool, int32_t* skipped,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------
  * Debug export of the block-table/window resolver the attention kernels use.
  * rows_out: int32 [n_q_total][n_cand]: for query j and candidate index i of
  * its sequence's window enumeration (causal: positions 0..seq_len-1; span:

@@ -42,6 +42,7 @@ EXPORTS = (
     "pkv_order_moves",
     "pkv_copy_cells_workspace_bytes",
     "pkv_kv_copy_cells",
+    "pkv_kv_store",
     "pkv_resolve_rows",
     "pkv_last_error",
     "pkv_version",
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
         "pkv_order_moves": (I32, [P, I32, P, P]),
         "pkv_copy_cells_workspace_bytes": (SZ, [P, I32, I64, I64]),
         "pkv_kv_copy_cells": (I32, [P, P, I32, I32, I32, I64, I64, P, I32, P, SZ, P]),
+        "pkv_kv_store": (I32, [SH, I32, I32, P, P, P, P, P, P, P, P, P]),
         "pkv_resolve_rows": (I32, [SH, I32, P, P, P, P, I32, I32, P, I32, P, P]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_char_p, []),
@@ -341,4 +343,61 @@ def kv_copy_cells(k_pool, v_pool, moves, workspace=None):
     ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=k_pool.device)
     _check(lib().pkv_kv_copy_cells(_ptr(k_pool), _ptr(v_pool), nb, bs, hkv, seg_k, seg_v, mv.ctypes.data, n,
                                    _ptr(ws), ws.numel(), _stream(k_pool)))
+    return k_pool, v_pool
+
+
+# ---------------------------------------------------------------------------
+# store
+
+
+def kv_store(k_new, v_new, positions, k_pool, v_pool, block_table, seq_ids=None, skipped=None):
+    """Write token t's rows k_new[t], v_new[t] ([n_tok, n_kv_heads, head_dim],
+    float32 or float16) into pool row table[s][p // bs] * bs + p % bs of each
+    pool (s = seq_ids[t], or t when seq_ids is None; p = positions[t]),
+    converted to the pool's format (q8_0 through the store quantizer).
+    v_new and v_pool may both be None.  Tokens without a destination are
+    left out and counted into ``skipped`` (a device int32 tensor of one
+    element, cleared by the caller) when it is given."""
+    torch = _torch()
+    if k_new.dtype not in (torch.float32, torch.float16):
+        raise TypeError("k_new must be float32 or float16")
+    if (v_new is None) != (v_pool is None):
+        raise ValueError("v_new and v_pool go together")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if t is not None and not t.is_contiguous():
+            raise TypeError(f"{name} must be contiguous")
+    if v_new is not None and (v_new.dtype != k_new.dtype or v_new.shape != k_new.shape):
+        raise TypeError("v_new must match k_new in dtype and shape")
+    if k_new.dim() != 3 or k_pool.dim() != 4:
+        raise TypeError("k_new is [n_tok, n_kv_heads, head_dim]; pools are [n_blocks, n_kv_heads, block_size, W]")
+    n_tok, hkv, hd = k_new.shape
+    nb, phkv, bs = k_pool.shape[:3]
+    if phkv != hkv:
+        raise ValueError("k_new and k_pool disagree on n_kv_heads")
+    if v_pool is not None and tuple(v_pool.shape[:3]) != (nb, hkv, bs):
+        raise ValueError("K and V pools must agree on (n_blocks, n_kv_heads, block_size)")
+    _i32(block_table, "block_table")
+    _i32(positions, "positions")
+    if positions.numel() != n_tok:
+        raise ValueError("positions must have one entry per token")
+    if seq_ids is not None:
+        _i32(seq_ids, "seq_ids")
+        if seq_ids.numel() != n_tok:
+            raise ValueError("seq_ids must have one entry per token")
+    if skipped is not None:
+        _i32(skipped, "skipped")
+    kf = _fmt_of(k_pool)
+    vf = _fmt_of(v_pool) if v_pool is not None else F16
+    for fmt, pool in ((kf, k_pool), (vf, v_pool)):
+        if pool is None:
+            continue
+        if pool.shape[3] * pool.element_size() != row_bytes(fmt, 1, hd):
+            raise ValueError(f"pool width {pool.shape[3]} does not hold head_dim {hd} in its format")
+    sh = Shape(n_seqs=block_table.shape[0], n_q_heads=hkv, n_kv_heads=hkv, head_dim=hd, block_size=bs,
+               n_pool_blocks=nb, max_blocks_per_seq=block_table.shape[1], q_fmt=F32, k_fmt=kf, v_fmt=vf,
+               scale=1.0, flags=0, split_tokens=0)
+    src = F32 if k_new.dtype == torch.float32 else F16
+    _check(lib().pkv_kv_store(ctypes.byref(sh), n_tok, src, _ptr(k_new), _ptr(v_new), _ptr(seq_ids),
+                              _ptr(positions), _ptr(block_table), _ptr(k_pool), _ptr(v_pool), _ptr(skipped),
+                              _stream(k_pool)))
     return k_pool, v_pool

@@ -563,4 +563,65 @@ pkv_status pkv_resolve_rows(const pkv_shape* sh, int32_t n_q_total, const int32_
   return ok();
 }
 
+pkv_status pkv_kv_store(const pkv_shape* sh, int32_t n_tok, int32_t src_fmt, const void* k_new,
+                        const void* v_new, const int32_t* seq_ids, const int32_t* positions,
+                        const int32_t* block_table, void* k_pool, void* v_pool, int32_t* skipped,
+                        void* stream) {
+  if (!sh) return fail(PKV_E_ARG, "shape is NULL");
+  if (n_tok < 0) return fail(PKV_E_ARG, "negative token count %d", n_tok);
+  if (sh->n_seqs < 0 || sh->n_kv_heads <= 0 || sh->block_size <= 0 || sh->n_pool_blocks <= 0 ||
+      sh->max_blocks_per_seq <= 0)
+    return fail(PKV_E_ARG,
+                "n_seqs %d must be >= 0 and n_kv_heads %d, block_size %d, n_pool_blocks %d, "
+                "max_blocks_per_seq %d positive",
+                sh->n_seqs, sh->n_kv_heads, sh->block_size, sh->n_pool_blocks,
+                sh->max_blocks_per_seq);
+  if (src_fmt != PKV_F32 && src_fmt != PKV_F16)
+    return fail(PKV_E_ARG, "source format must be f32 or f16, got %s", fmt_name(src_fmt));
+  for (int f : {sh->k_fmt, sh->v_fmt})
+    if (f != PKV_F32 && f != PKV_F16 && f != PKV_Q8_0)
+      return fail(PKV_E_ARG, "unknown KV format value %d", f);
+  const int hd = sh->head_dim;
+  if (hd != 32 && hd != 64 && hd != 128 && hd != 256)
+    return fail(PKV_E_UNSUPPORTED, "store supports head_dim 32, 64, 128 and 256, not %d", hd);
+  if ((int64_t)n_tok * sh->n_kv_heads > INT32_MAX)
+    return fail(PKV_E_ARG, "n_tok * n_kv_heads exceeds 2^31 - 1");
+  if ((int64_t)sh->n_pool_blocks * sh->n_kv_heads * sh->block_size > INT32_MAX)
+    return fail(PKV_E_ARG, "n_pool_blocks * n_kv_heads * block_size exceeds 2^31 - 1");
+  if ((int64_t)sh->max_blocks_per_seq * sh->block_size > INT32_MAX)
+    return fail(PKV_E_ARG, "max_blocks_per_seq * block_size overflows int32");
+  if (!seq_ids && n_tok > sh->n_seqs)
+    return fail(PKV_E_ARG, "without seq_ids token t belongs to sequence t: n_tok %d > n_seqs %d",
+                n_tok, sh->n_seqs);
+  if (n_tok == 0) return ok();  // nothing is read, so no pointer is checked
+  if (!k_new || !k_pool || !positions || !block_table)
+    return fail(PKV_E_ARG, "k_new, k_pool, positions and block_table must be non-NULL");
+  if ((v_new == nullptr) != (v_pool == nullptr))
+    return fail(PKV_E_ARG, "v_new and v_pool must both be given or both be NULL");
+  for (const void* p : {k_new, v_new, (const void*)k_pool, (const void*)v_pool})
+    if (((uintptr_t)p) % 16) return fail(PKV_E_ARG, "sources and pools must be 16-byte aligned");
+  pkv::StoreArgs a{};
+  a.src[0] = (const unsigned char*)k_new;
+  a.src[1] = (const unsigned char*)v_new;
+  a.pool[0] = (unsigned char*)k_pool;
+  a.pool[1] = (unsigned char*)v_pool;
+  a.fmt[0] = sh->k_fmt;
+  a.fmt[1] = sh->v_fmt;
+  a.seq_ids = seq_ids;
+  a.pos = positions;
+  a.table = block_table;
+  a.skipped = skipped;
+  a.n_tok = n_tok;
+  a.n_seqs = sh->n_seqs;
+  a.n_kv_heads = sh->n_kv_heads;
+  a.block_size = sh->block_size;
+  a.n_pool_blocks = sh->n_pool_blocks;
+  a.max_blocks = sh->max_blocks_per_seq;
+  bool found = false;
+  hipError_t e = pkv::launch_store(a, src_fmt, hd, (hipStream_t)stream, &found);
+  if (!found) return fail(PKV_E_UNSUPPORTED, "no store kernel for head_dim %d", hd);
+  if (e != hipSuccess) return device_fail(e, "store launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -209,4 +209,18 @@ hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stag
                             const int32_t* pairs, int32_t n_pairs, hipStream_t st);
 hipError_t launch_zero_words(int32_t* p, int n, hipStream_t st);
 
+// Store of new K/V rows through the block table (pool[1] may be null).
+struct StoreArgs {
+  const unsigned char* src[2];  // [n_tok][n_kv_heads][head_dim] of the source type
+  unsigned char* pool[2];       // [n_pool_blocks][n_kv_heads][block_size][seg]
+  int32_t fmt[2];               // pool formats
+  const int32_t* seq_ids;       // [n_tok] or null: token t belongs to sequence t
+  const int32_t* pos;           // [n_tok]
+  const int32_t* table;         // [n_seqs][max_blocks]
+  int32_t* skipped;             // tokens not stored are added here, or null
+  int32_t n_tok, n_seqs, n_kv_heads, block_size, n_pool_blocks, max_blocks;
+};
+// Grid: ceil(n_tok * n_kv_heads / units per workgroup) x 256 threads.
+hipError_t launch_store(const StoreArgs& a, int src_fmt, int hd, hipStream_t st, bool* found);
+
 }  // namespace pkv

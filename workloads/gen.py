@@ -325,6 +325,95 @@ def make_moves(seed: int = 55, n_moves: int = 10000, n_rows: int = 1 << 21,
     return MoveSet(seed=seed, n_rows=n_rows, moves=out)
 
 
+@dataclasses.dataclass
+class StoreSet:
+    """New K/V rows to store: token t belongs to sequence seq_ids[t] and sits
+    at position pos[t]; its rows go to the pool through block_table."""
+    name: str
+    seed: int
+    n_kv_heads: int
+    head_dim: int
+    block_size: int
+    n_pool_blocks: int
+    src_fmt: str  # "f32" | "f16": type of the new rows
+    k_fmt: str
+    v_fmt: str
+    block_table: np.ndarray  # int32 [S, MB]; -1 marks a hole
+    seq_ids: np.ndarray  # int32 [n_tok]
+    pos: np.ndarray  # int32 [n_tok]
+
+    @property
+    def n_tok(self) -> int:
+        return int(len(self.pos))
+
+    @property
+    def n_seqs(self) -> int:
+        return int(self.block_table.shape[0])
+
+
+def make_store(seed: int, n_seqs: int, n_kv_heads: int, head_dim: int, block_size: int, n_pool_blocks: int,
+               max_blocks: int, tok=(1, 40), src_fmt: str = "f16", k_fmt: str = "q8_0", v_fmt: str = "f16",
+               hole_frac: float = 0.0, shuffle: bool = True) -> StoreSet:
+    """Each sequence owns distinct pool blocks from one permutation (its whole
+    table is filled, then hole_frac of the entries become holes) and receives
+    a run of n_s ~ U{tok} new tokens at positions [p0, p0 + n_s), p0 drawn so
+    the run fits the table: a prefill chunk, or a decode append when n_s = 1.
+    Tokens are listed in random order when shuffle."""
+    rng = np.random.default_rng(seed)
+    if n_seqs * max_blocks > n_pool_blocks:
+        raise ValueError("pool too small for the tables")
+    perm = rng.permutation(n_pool_blocks)[: n_seqs * max_blocks]
+    table = perm.reshape(n_seqs, max_blocks).astype(np.int32)
+    if hole_frac > 0:
+        table[rng.random(table.shape) < hole_frac] = INVALID_BLOCK
+    cap = max_blocks * block_size
+    seq_ids, pos = [], []
+    for s_ in range(n_seqs):
+        n = int(rng.integers(tok[0], min(tok[1], cap) + 1))
+        p0 = int(rng.integers(0, cap - n + 1))
+        seq_ids.append(np.full(n, s_, dtype=np.int32))
+        pos.append(np.arange(p0, p0 + n, dtype=np.int32))
+    seq_ids = np.concatenate(seq_ids)
+    pos = np.concatenate(pos)
+    if shuffle:
+        order = rng.permutation(len(pos))
+        seq_ids, pos = seq_ids[order], pos[order]
+    return StoreSet(name="store", seed=seed, n_kv_heads=n_kv_heads, head_dim=head_dim, block_size=block_size,
+                    n_pool_blocks=n_pool_blocks, src_fmt=src_fmt, k_fmt=k_fmt, v_fmt=v_fmt, block_table=table,
+                    seq_ids=seq_ids, pos=pos)
+
+
+def store_of_workload(w: Workload, src_fmt: str = "f16") -> StoreSet:
+    """The store that fills workload w's pools: every position [0, seq_len)
+    of every sequence, in sequence order (the prefill of the whole context)."""
+    seq_ids = np.concatenate([np.full(int(L), s_, dtype=np.int32) for s_, L in enumerate(w.seq_lens)])
+    pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in w.seq_lens])
+    return StoreSet(name=f"store-{w.name}", seed=w.seed, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                    block_size=w.block_size, n_pool_blocks=w.n_pool_blocks, src_fmt=src_fmt, k_fmt=w.k_fmt,
+                    v_fmt=w.v_fmt, block_table=w.block_table.copy(), seq_ids=seq_ids, pos=pos)
+
+
+def store_values(st: StoreSet, device="cpu", seed_offset: int = 0):
+    """New rows (k_new, v_new) [n_tok, n_kv_heads, head_dim] in st.src_fmt:
+    N(0, 1) float32 draws from a torch.Generator seeded with st.seed on the
+    target device, cast to float16 when the source is f16."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(1000003 * st.seed + 17 + seed_offset)
+    shape = (st.n_tok, st.n_kv_heads, st.head_dim)
+    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if st.src_fmt == "f16":
+        k, v = k.half(), v.half()
+    return k.contiguous(), v.contiguous()
+
+
+def pool_width(fmt: str, head_dim: int) -> int:
+    """Last-axis length of a pool tensor: head_dim values, or q8_0 bytes."""
+    return q8_0_seg_bytes(head_dim) if fmt == "q8_0" else head_dim
+
+
 # ----------------------------------------------------------------------------
 # values
 
