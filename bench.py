@@ -24,7 +24,7 @@ size used to scale the HBM byte counters.
 Counter summary (turns two rocprofv3 --pmc runs, FETCH_SIZE then WRITE_SIZE,
 of a workload and of the calibration copy into bytes per launch):
 
-    python bench.py --pmc-summary KERNEL FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
+    python bench.py --pmc-summary WORKLOAD KERNEL FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
 """
 
 from __future__ import annotations
@@ -42,11 +42,18 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 CALIB_BYTES = 4 << 30  # bytes read and bytes written by one calibration copy
-# Sources that determine the decode split kernel's code; a stored counter
-# summary only applies while their hash is unchanged.
-DECODE_SOURCES = ("include/pkv.h", "paged_kv_cache_table_amd/csrc/pkv_internal.hpp",
-                  "paged_kv_cache_table_amd/csrc/decode_impl.hpp", "paged_kv_cache_table_amd/csrc/decode_f16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_7b_class.traffic.json")
+# Counter summaries per workload: the committed file and the sources that
+# determine the measured kernel's code; a summary only applies while their
+# hash is unchanged.
+_CSRC = "paged_kv_cache_table_amd/csrc/"
+TRAFFIC = {
+    "decode3": ("profiles/decode_split_7b_class.traffic.json",
+                ("include/pkv.h", _CSRC + "pkv_internal.hpp", _CSRC + "decode_impl.hpp", _CSRC + "decode_f16.hip")),
+    "store4": ("profiles/store_w4.traffic.json",
+               ("include/pkv.h", _CSRC + "pkv_internal.hpp", _CSRC + "store.hip")),
+    "prefill4": ("profiles/prefill_window_w4.traffic.json",
+                 ("include/pkv.h", _CSRC + "pkv_internal.hpp", _CSRC + "prefill.hip")),
+}
 MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + queries/s"
 
@@ -132,15 +139,17 @@ def sources_hash(paths) -> str:
     return h.hexdigest()
 
 
-def stored_traffic():
-    """HBM bytes per launch of the decode split kernel from the committed
-    counter summary, or None if absent or taken on other kernel sources."""
+def stored_traffic(workload):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed counter summary, or None if absent or taken on other kernel
+    sources."""
+    path, sources = TRAFFIC[workload]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, path)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("sources_sha256") != sources_hash(DECODE_SOURCES):
+    if t.get("sources_sha256") != sources_hash(sources):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -153,19 +162,25 @@ def _pmc_mean(path, kernel_substr, counter):
     return sum(vals) / len(vals), len(vals)
 
 
-def pmc_summary(kernel, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+def pmc_summary(workload, kernel, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of `kernel`, each scaled by
     the factor that maps the same counter to the known bytes of the
-    calibration copy."""
-    f_kib, nf = _pmc_mean(fetch_csv, kernel, "FETCH_SIZE")
-    w_kib, nw = _pmc_mean(write_csv, kernel, "WRITE_SIZE")
+    calibration copy.  `kernel` may name several kernels joined by '+' (the
+    launches of one call): their per-dispatch means are added."""
+    f_kib = w_kib = 0.0
+    nf = nw = 0
+    for k in kernel.split("+"):
+        f, n1 = _pmc_mean(fetch_csv, k, "FETCH_SIZE")
+        w_, n2 = _pmc_mean(write_csv, k, "WRITE_SIZE")
+        f_kib, w_kib, nf, nw = f_kib + f, w_kib + w_, max(nf, n1), max(nw, n2)
     cf_kib, _ = _pmc_mean(cal_fetch_csv, "copy", "FETCH_SIZE")
     cw_kib, _ = _pmc_mean(cal_write_csv, "copy", "WRITE_SIZE")
     f_scale = CALIB_BYTES / (cf_kib * 1024)
     w_scale = CALIB_BYTES / (cw_kib * 1024)
     out = {
+        "workload": workload,
         "kernel": kernel,
-        "sources_sha256": sources_hash(DECODE_SOURCES),
+        "sources_sha256": sources_hash(TRAFFIC[workload][1]),
         "fetch_kib_per_dispatch": round(f_kib, 1), "fetch_dispatches": nf,
         "write_kib_per_dispatch": round(w_kib, 1), "write_dispatches": nw,
         "calib_fetch_kib": round(cf_kib, 1), "calib_write_kib": round(cw_kib, 1),
@@ -174,6 +189,20 @@ def pmc_summary(kernel, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     }
     print(json.dumps(out, indent=2))
     return 0
+
+
+class ColdCache:
+    """Evicts L2 and the 256 MB Infinity Cache between timed steps by reading
+    a 1 GiB buffer (filled once): the caches end up holding clean lines, so
+    no write-back of unrelated dirty data lands inside the timed region."""
+
+    def __init__(self):
+        import torch
+
+        self.buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+
+    def __call__(self):
+        self.buf.sum()
 
 
 def run_calib(args):
@@ -283,7 +312,7 @@ def run_decode(cfg, args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic() if cfg == 3 and not args.split else None,
+            "traffic": stored_traffic("decode3") if cfg == 3 and not args.split else None,
             "algorithmic_bytes": int(alg),
         },
     }
@@ -326,7 +355,7 @@ def run_prefill(args):
     max_q = int(np.max(np.diff(w.cu_q)))
     out = torch.empty((w.n_queries, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.n_queries, w.n_q_heads), dtype=torch.float32, device="cuda")
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # evicts L2 and the 256 MB MALL
+    flush = ColdCache()  # the whole input (0.16 GB of K/V) would otherwise sit in the 256 MB cache
 
     def call():
         pkv.paged_attn_prefill_window(q, dev["cu_q"], dev["q_pos"], k, v, dev["table"], dev["lens"], w.scale, max_q,
@@ -338,7 +367,7 @@ def run_prefill(args):
     stream = torch.cuda.current_stream()
     times = []
     for _ in range(args.steps):
-        flush.fill_(1)  # the whole input (0.16 GB of K/V) would otherwise sit in the 256 MB cache
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         call()
@@ -357,9 +386,10 @@ def run_prefill(args):
         "config": {"workload": f"{w.name}: {w.n_seqs} seqs x {max_q} queries, 32 q / 8 kv heads, hd 128, block 32, "
                                "K q8_0, V f16; half one span, half 4 runs; causal in window; cache flushed per step",
                    "visible_pairs": pairs, "flops": flops, "kv_bytes": kv_bytes},
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "prefill_order_kernel + prefill_kernel + prefill_merge_kernel (one call)",
+                     "achieved": round(tflops, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None, "hbm_GBps": round(io_bytes / (ms * 1e-3) / 1e9, 1),
+                     "traffic": stored_traffic("prefill4"), "hbm_GBps": round(io_bytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
 
@@ -423,7 +453,7 @@ def run_store(args):
     table = torch.from_numpy(st.block_table).cuda()
     pos = torch.from_numpy(st.pos).cuda()
     sid = torch.from_numpy(st.seq_ids).cuda()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = ColdCache()
 
     def call():
         pkv.kv_store(k_new, v_new, pos, kp, vp, table, seq_ids=sid)
@@ -434,7 +464,7 @@ def run_store(args):
     stream = torch.cuda.current_stream()
     times = []
     for _ in range(args.steps):
-        flush.fill_(1)
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         call()
@@ -460,7 +490,8 @@ def run_store(args):
                    "tokens": n, "bytes": total},
         "tokens_per_s": round(n / (ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "kernel": "store_kernel", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic("store4"),
+                     "algorithmic_bytes": int(total)},
     }
 
 
@@ -471,7 +502,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode3",
                     choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "calib"])
-    ap.add_argument("--pmc-summary", nargs=5, metavar=("KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
+    ap.add_argument("--pmc-summary", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
     ap.add_argument("--split", type=int, default=0, help="decode split size in tokens (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)

@@ -19,7 +19,10 @@
 // HD/8 lanes share a unit, 8 consecutive values per lane, so a wave reads
 // 64 * 8 consecutive source values.  Each thread carries kSteps units of K
 // and of V through the loads before it converts any, to keep enough bytes in
-// flight.  f16/f32 pools take one 16-byte store per lane and pool; a q8_0
+// flight (two steps measured best: more steps cost occupancy).  Sources are
+// read once, with non-temporal loads that keep them from displacing the
+// pool lines being written (plain stores measured faster than non-temporal
+// ones).  f16/f32 pools take one 16-byte store per lane and pool; a q8_0
 // segment (34-byte blocks, only 2-byte aligned inside) is assembled in LDS
 // and written out as whole 4-byte words.
 #include "pkv_internal.hpp"
@@ -30,7 +33,7 @@ namespace {
 
 constexpr int kStoreThreads = 256;
 constexpr int kStoreWaves = kStoreThreads / kWave;
-constexpr int kSteps = 4;
+constexpr int kSteps = 2;
 
 template <int HD>
 struct StoreGeom {
@@ -43,39 +46,31 @@ struct StoreGeom {
   static constexpr int WAVE_UNITS = UW * kSteps;         // units a wave stages
 };
 
-// Eight source values of one lane as floats.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Eight source values of one lane as floats (16-byte non-temporal loads).
 template <typename S>
 struct Src8;
 template <>
 struct Src8<_Float16> {
-  uint4 w;
-  __device__ void load(const unsigned char* p) { w = *(const uint4*)p; }
-  __device__ void zero() { w = make_uint4(0, 0, 0, 0); }
+  u32x4 w;
+  __device__ void load(const unsigned char* p) { w = __builtin_nontemporal_load((const u32x4*)p); }
+  __device__ void zero() { w = u32x4{0, 0, 0, 0}; }
   __device__ float at(int i) const {
-    const uint32_t x = i < 2 ? w.x : i < 4 ? w.y : i < 6 ? w.z : w.w;
+    const uint32_t x = w[i / 2];
     return (i & 1) ? h2f_hi(x) : h2f_lo(x);
   }
 };
 template <>
 struct Src8<float> {
-  float4 a, b;
+  f32x4 a, b;
   __device__ void load(const unsigned char* p) {
-    a = ((const float4*)p)[0];
-    b = ((const float4*)p)[1];
+    a = __builtin_nontemporal_load((const f32x4*)p);
+    b = __builtin_nontemporal_load((const f32x4*)p + 1);
   }
-  __device__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
-  __device__ float at(int i) const {
-    switch (i) {
-      case 0: return a.x;
-      case 1: return a.y;
-      case 2: return a.z;
-      case 3: return a.w;
-      case 4: return b.x;
-      case 5: return b.y;
-      case 6: return b.z;
-      default: return b.w;
-    }
-  }
+  __device__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
 };
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
