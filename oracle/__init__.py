@@ -21,6 +21,10 @@ written from the source pages directly:
 * "KV Cache Design", section 3: the store's q8_0 quantizer (scale amax/127
   kept as f16, codes rounded to nearest, ties to even); the store writes a
   token's rows through the block table.
+* "Tiered KV cache — architecture", section "The paged-attention block
+  model", and "KV Cache Design", sections 1-2: the copy-on-write block pool
+  (forks share blocks by reference count; a write into a shared block
+  copies it first, so readers of the shared prefix see no change).
 
 Arithmetic is float64 numpy; byte work is exact.  Readings of points the
 pages leave open are stated in the docstrings where they are used.
@@ -42,3 +46,4 @@ from .attention import (  # noqa: F401
 )
 from .moves import order_moves, copy_cells, copy_cells_rowwise, provenance  # noqa: F401
 from .store import quantize_q8_0, encode_rows, destination_rows, store_rows  # noqa: F401
+from .cow import BlockPoolModel, copy_blocks  # noqa: F401
