@@ -18,7 +18,7 @@ resident in HBM.  Prints one JSON line:
   workload on this host.
 
 Other workloads (for the record; the default is the headline): decode1,
-decode2, decode5, prefill4, copy5b, store4; and calib, a plain device copy of known
+decode2, decode5, prefill4, copy5b, store4, cow3; and calib, a plain device copy of known
 size used to scale the HBM byte counters.
 
 Counter summary (turns two rocprofv3 --pmc runs, FETCH_SIZE then WRITE_SIZE,
@@ -495,13 +495,133 @@ def run_store(args):
     }
 
 
+def run_cow(args):
+    """Copy-on-write fork step: 256 parents (7B-class layer shape: 8 kv heads,
+    hd 128, block 16, f16 K/V) of 1000..8000 tokens, each forked three times;
+    in one step all 1024 sequences append one token.  Every fork whose
+    shared last block is partial must copy it first.  Timed per step: host
+    planning (prepare_writes), the upload of its ops, cow_apply (block
+    copies + device table patches) and the store of the 1024 rows; the
+    copy kernel is also timed alone for its roofline."""
+    import torch
+
+    import paged_kv_cache_table_amd as pkv
+
+    rng = np.random.default_rng(3)
+    n_par, fan, hkv, hd, bs = 256, 4, 8, 128, 16
+    n_seqs = n_par * fan
+    L = rng.integers(1000, 8001, size=n_par).astype(np.int32)
+    max_blocks = 8192 // bs + 2
+    n_blocks = int(np.sum((L + bs - 1) // bs)) * 2 + 4096
+    log(f"[bench] cow: {n_par} parents x {fan} members, {n_blocks} blocks per pool")
+    pool = pkv.BlockPool(n_blocks, n_seqs, max_blocks, bs)
+    k = torch.zeros((n_blocks, hkv, bs, hd), dtype=torch.float16, device="cuda")
+    v = torch.zeros_like(k)
+    table = torch.full((n_seqs, max_blocks), -1, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    # parents: one prefill store each (fresh blocks only)
+    pseqs = np.arange(0, n_seqs, fan, dtype=np.int32)
+    ops = pool.prepare_writes(pseqs, np.zeros(n_par, dtype=np.int32), L)
+    pkv.cow_apply(k, v, ops, table)
+    n_tok = int(L.sum())
+    sid = torch.from_numpy(np.repeat(pseqs, L)).cuda()
+    pos = torch.from_numpy(np.concatenate([np.arange(x, dtype=np.int32) for x in L])).cuda()
+    for lo in range(0, n_tok, 1 << 16):
+        hi = min(n_tok, lo + (1 << 16))
+        rows = torch.randn((hi - lo, hkv, hd), generator=g, device="cuda").half()
+        pkv.kv_store(rows, rows, pos[lo:hi], k, v, table, seq_ids=sid[lo:hi])
+    step_rows = torch.randn((n_seqs, hkv, hd), generator=g, device="cuda").half()
+    all_seqs = np.arange(n_seqs, dtype=np.int32)
+    step_pos_h = np.repeat(L, fan).astype(np.int32)
+    step_pos = torch.from_numpy(step_pos_h).cuda()
+    step_sid = torch.from_numpy(all_seqs).cuda()
+    ones = np.ones(n_seqs, dtype=np.int32)
+    ops_host = torch.empty((4 * n_seqs, 3), dtype=torch.int32).pin_memory()
+    ops_dev = torch.empty((4 * n_seqs, 3), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def reset():
+        """Untimed: drop the members' step tokens and forks, fork again."""
+        for p in range(n_par):
+            base = fan * p
+            pool.remove(base, int(L[p]), int(L[p]) + 1)
+            for m in range(1, fan):
+                pool.remove(base + m, 0, 1 << 30)
+            for m in range(1, fan):
+                pool.fork(base, base + m)
+        t, _ = pool.export()
+        table.copy_(torch.from_numpy(t))
+        torch.cuda.synchronize()
+
+    def step(ev=None):
+        ops = pool.prepare_writes(all_seqs, step_pos_h, ones)
+        n = len(ops)
+        ops_host[:n].numpy()[:] = ops
+        ops_dev[:n].copy_(ops_host[:n], non_blocking=True)
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.cow_apply(k, v, ops_dev[:n], table)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.kv_store(step_rows, step_rows, step_pos, k, v, table, seq_ids=step_sid)
+        return ops
+
+    for p in range(n_par):
+        for m in range(1, fan):
+            pool.fork(fan * p, fan * p + m)
+    t, _ = pool.export()
+    table.copy_(torch.from_numpy(t))
+    for _ in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        reset()
+    walls = []
+    n_copies = 0
+    for _ in range(args.steps):  # wall clock: host plan + upload + both kernels
+        t0 = time.perf_counter()
+        ops = step()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        n_copies = int(np.count_nonzero(ops[:, 0] >= 0))
+        reset()
+    kern, dev = [], []
+    for _ in range(args.steps):  # device time: the GPU is kept busy while the host enqueues
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda._sleep(400000)
+        step(ev)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        kern.append(ev[0].elapsed_time(ev[1]))
+        dev.append(ev[0].elapsed_time(ev[2]))
+        reset()
+    wall = float(np.mean(walls))
+    kms = float(np.mean(kern))
+    block_bytes = hkv * bs * hd * 2
+    copy_bytes = 2 * n_copies * 2 * block_bytes  # K and V blocks, read + written
+    gbs = copy_bytes / (kms * 1e-3) / 1e9
+    return {
+        "metric": "copy-on-write fork step: sequences appended per second (host plan + block copies + store)",
+        "value": round(n_seqs / wall, 1), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{n_par} parents of 1000..8000 tokens x {fan} members (8 kv heads, hd 128, block 16, "
+                               f"f16 K/V); every member appends one token; wall clock per step",
+                   "sequences": n_seqs, "block_copies": n_copies, "copy_bytes": copy_bytes},
+        "roofline": {"bound": "hbm", "kernel": "cow_apply_kernel", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms": round(kms, 5)},
+        "device_ms_per_step": round(float(np.mean(dev)), 5),
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode3",
-                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "calib"])
+                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "cow3", "calib"])
     ap.add_argument("--pmc-summary", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
     ap.add_argument("--split", type=int, default=0, help="decode split size in tokens (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -533,6 +653,8 @@ def main(argv=None):
         res = run_prefill(args)
     elif args.workload == "store4":
         res = run_store(args)
+    elif args.workload == "cow3":
+        res = run_cow(args)
     elif args.workload == "copy5b":
         res = run_copy(args)
     else:

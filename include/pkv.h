@@ -61,7 +61,8 @@ typedef enum {
   PKV_E_ARG = 1,         /* malformed argument (null, negative, mismatch) */
   PKV_E_UNSUPPORTED = 2, /* well formed but outside the dispatch table   */
   PKV_E_WORKSPACE = 3,   /* workspace missing or too small                */
-  PKV_E_DEVICE = 4       /* a HIP call failed                             */
+  PKV_E_DEVICE = 4,      /* a HIP call failed                             */
+  PKV_E_CAPACITY = 5     /* the block pool has too few free blocks        */
 } pkv_status;
 
 /* KV storage formats ("KV Cache Design", section 3: f32, f16, q8_0). */
@@ -269,6 +270,92 @@ pkv_status pkv_kv_store(const pkv_shape* shape, int32_t n_tok, int32_t src_fmt, 
                         const void* v_new, const int32_t* seq_ids, const int32_t* positions,
                         const int32_t* block_table, void* k_pool, void* v_pool, int32_t* skipped,
                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Copy-on-write block pool (host).  Forking a sequence only raises the
+ * reference counts of its blocks and copies its table; no K/V bytes move
+ * until a fork writes ("Tiered KV cache — architecture", section "The
+ * paged-attention block model").  A store may never land in a block another
+ * sequence still reads, so a write into a shared block first copies it into
+ * a fresh block ("KV Cache Design", sections 1 and 2); readers of the shared
+ * prefix see no change.  A partial removal wipes whole logical blocks (their
+ * entries become PKV_INVALID_BLOCK_ID).  The pool also keeps a watermark of
+ * blocks that admission checks leave free (the same page's file list names a
+ * physical allocator with reference counts and a watermark).
+ *
+ * The pool owns only host memory: per-block reference counts, the block
+ * tables [n_seqs][max_blocks_per_seq] and sequence lengths.  Callers export
+ * the tables to the device (pkv_pool_export) for attention and store.  Not
+ * internally locked; one thread mutates a pool at a time.
+ *
+ * Rules:
+ *  - allocation takes the free block with the smallest id; a block is free
+ *    exactly when no table entry names it;
+ *  - fork(src, dst, n): dst must be empty; it takes src's first
+ *    ceil(n / block_size) entries (holes stay holes) and length n (n < 0:
+ *    src's length); each block it names gains a reference;
+ *  - remove(seq, p0, p1) on [p0, p1) clipped to [0, length): if it reaches
+ *    the end, the length becomes p0 and every logical block starting at or
+ *    after p0 is released; otherwise each logical block lying wholly inside
+ *    is released and becomes a hole (removal is block-granular);
+ *  - prepare_writes before writing positions [p0, p0 + count) of seq
+ *    (p0 <= length, no gap), for each write in order and each logical block
+ *    it touches: a block only this sequence names is written in place; a
+ *    shared block is copied into a fresh block (the pair (src, dst) is
+ *    returned, the shared block loses a reference); an empty entry gets a
+ *    fresh block, whose rows other than the written ones hold whatever the
+ *    pool held.  The length becomes max(length, p0 + count).  The returned
+ *    ops must run (pkv_cow_apply) before the rows are stored; their copies
+ *    read the blocks as they were before the batch.  The whole batch is checked
+ *    before anything changes: a refused call changes nothing.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_block_pool pkv_block_pool;
+
+pkv_status pkv_pool_create(int32_t n_blocks, int32_t n_seqs, int32_t max_blocks_per_seq,
+                           int32_t block_size, int32_t watermark, pkv_block_pool** out);
+void pkv_pool_destroy(pkv_block_pool* pool);
+
+/* Free blocks; whether n more blocks can be taken with the watermark still
+ * free (1/0); references to a block (-1 outside the pool); a sequence's
+ * length (-1 outside the pool). */
+int32_t pkv_pool_free_blocks(const pkv_block_pool* pool);
+int32_t pkv_pool_can_allocate(const pkv_block_pool* pool, int32_t n);
+int32_t pkv_pool_refcount(const pkv_block_pool* pool, int32_t block);
+int32_t pkv_pool_seq_len(const pkv_block_pool* pool, int32_t seq);
+
+pkv_status pkv_pool_fork(pkv_block_pool* pool, int32_t src, int32_t dst, int32_t n_tokens);
+pkv_status pkv_pool_remove(pkv_block_pool* pool, int32_t seq, int32_t p0, int32_t p1);
+
+/* n writes (host arrays seqs, p0s, counts; counts <= 0 are skipped).
+ * ops_out: host int32 [max_ops][3] receiving one op per table entry the
+ * writes change, in order: (src, dst, entry) = (the shared block to copy,
+ * or -1 for a fresh block with nothing to copy; the new block; the entry's
+ * index seq * max_blocks_per_seq + logical block).  *n_ops their number.
+ * PKV_E_CAPACITY when the pool lacks free blocks, PKV_E_WORKSPACE when
+ * max_ops is too small (at most one op per logical block a write touches). */
+pkv_status pkv_pool_prepare_writes(pkv_block_pool* pool, int32_t n, const int32_t* seqs,
+                                   const int32_t* p0s, const int32_t* counts, int32_t* ops_out,
+                                   int32_t max_ops, int32_t* n_ops);
+
+/* Host copies of the tables (int32 [n_seqs][max_blocks_per_seq]) and, if
+ * lens_out is not NULL, the lengths (int32 [n_seqs]). */
+pkv_status pkv_pool_export(const pkv_block_pool* pool, int32_t* table_out, int32_t* lens_out);
+
+/* Device: apply prepare_writes' ops (device int32 [n][3]).  For each op,
+ * copy block src (when src >= 0) to block dst in k_pool and (if not NULL)
+ * v_pool, both [n_pool_blocks][...] with k_block_bytes / v_block_bytes per
+ * block (n_kv_heads * block_size * seg; multiples of 4; pools 16-byte
+ * aligned), and, when table is not NULL, set table[entry] = dst (table:
+ * device int32 of table_entries entries, the block tables [n_seqs]
+ * [max_blocks_per_seq] that attention and store read).  An op whose src or
+ * dst lies outside [0, n_pool_blocks), or with src == dst, copies nothing;
+ * an entry outside the table is not patched.  Sources and destinations must
+ * be disjoint, destinations distinct and entries distinct (prepare_writes
+ * guarantees all three); otherwise the result is unspecified.
+ * Run it before storing the batch's rows. */
+pkv_status pkv_cow_apply(void* k_pool, void* v_pool, int32_t n_pool_blocks, int64_t k_block_bytes,
+                         int64_t v_block_bytes, const int32_t* ops, int32_t n, int32_t* table,
+                         int64_t table_entries, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Debug export of the block-table/window resolver the attention kernels use.

@@ -27,7 +27,8 @@ FLAG_CHECKED = 1
 INVALID_BLOCK_ID = -1
 KV_MAP_MAX_SPANS = 8
 
-STATUS = {0: "PKV_OK", 1: "PKV_E_ARG", 2: "PKV_E_UNSUPPORTED", 3: "PKV_E_WORKSPACE", 4: "PKV_E_DEVICE"}
+STATUS = {0: "PKV_OK", 1: "PKV_E_ARG", 2: "PKV_E_UNSUPPORTED", 3: "PKV_E_WORKSPACE", 4: "PKV_E_DEVICE",
+          5: "PKV_E_CAPACITY"}
 
 # Every symbol include/pkv.h declares.
 EXPORTS = (
@@ -43,6 +44,17 @@ EXPORTS = (
     "pkv_copy_cells_workspace_bytes",
     "pkv_kv_copy_cells",
     "pkv_kv_store",
+    "pkv_pool_create",
+    "pkv_pool_destroy",
+    "pkv_pool_free_blocks",
+    "pkv_pool_can_allocate",
+    "pkv_pool_refcount",
+    "pkv_pool_seq_len",
+    "pkv_pool_fork",
+    "pkv_pool_remove",
+    "pkv_pool_prepare_writes",
+    "pkv_pool_export",
+    "pkv_cow_apply",
     "pkv_resolve_rows",
     "pkv_last_error",
     "pkv_version",
@@ -100,6 +112,17 @@ def lib() -> ctypes.CDLL:
         "pkv_copy_cells_workspace_bytes": (SZ, [P, I32, I64, I64]),
         "pkv_kv_copy_cells": (I32, [P, P, I32, I32, I32, I64, I64, P, I32, P, SZ, P]),
         "pkv_kv_store": (I32, [SH, I32, I32, P, P, P, P, P, P, P, P, P]),
+        "pkv_pool_create": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(P)]),
+        "pkv_pool_destroy": (None, [P]),
+        "pkv_pool_free_blocks": (I32, [P]),
+        "pkv_pool_can_allocate": (I32, [P, I32]),
+        "pkv_pool_refcount": (I32, [P, I32]),
+        "pkv_pool_seq_len": (I32, [P, I32]),
+        "pkv_pool_fork": (I32, [P, I32, I32, I32]),
+        "pkv_pool_remove": (I32, [P, I32, I32, I32]),
+        "pkv_pool_prepare_writes": (I32, [P, I32, P, P, P, P, I32, P]),
+        "pkv_pool_export": (I32, [P, P, P]),
+        "pkv_cow_apply": (I32, [P, P, I32, I64, I64, P, I32, P, I64, P]),
         "pkv_resolve_rows": (I32, [SH, I32, P, P, P, P, I32, I32, P, I32, P, P]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_char_p, []),
@@ -400,4 +423,106 @@ def kv_store(k_new, v_new, positions, k_pool, v_pool, block_table, seq_ids=None,
     _check(lib().pkv_kv_store(ctypes.byref(sh), n_tok, src, _ptr(k_new), _ptr(v_new), _ptr(seq_ids),
                               _ptr(positions), _ptr(block_table), _ptr(k_pool), _ptr(v_pool), _ptr(skipped),
                               _stream(k_pool)))
+    return k_pool, v_pool
+
+
+# ---------------------------------------------------------------------------
+# copy-on-write block pool
+
+
+class BlockPool:
+    """Host block pool with reference counts (the library's pkv_block_pool):
+    fork shares blocks, prepare_writes makes the blocks a write touches
+    private and returns the block copies that must run first."""
+
+    def __init__(self, n_blocks: int, n_seqs: int, max_blocks_per_seq: int, block_size: int, watermark: int = 0):
+        self._h = ctypes.c_void_p()
+        _check(lib().pkv_pool_create(n_blocks, n_seqs, max_blocks_per_seq, block_size, watermark,
+                                     ctypes.byref(self._h)))
+        self.n_blocks, self.n_seqs, self.max_blocks, self.block_size = n_blocks, n_seqs, max_blocks_per_seq, block_size
+
+    def close(self):
+        if self._h:
+            lib().pkv_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+    def free_blocks(self) -> int:
+        return int(lib().pkv_pool_free_blocks(self._h))
+
+    def can_allocate(self, n: int) -> bool:
+        return bool(lib().pkv_pool_can_allocate(self._h, n))
+
+    def refcount(self, block: int) -> int:
+        return int(lib().pkv_pool_refcount(self._h, block))
+
+    def seq_len(self, seq: int) -> int:
+        return int(lib().pkv_pool_seq_len(self._h, seq))
+
+    def fork(self, src: int, dst: int, n_tokens: int = -1):
+        _check(lib().pkv_pool_fork(self._h, src, dst, n_tokens))
+
+    def remove(self, seq: int, p0: int, p1: int):
+        _check(lib().pkv_pool_remove(self._h, seq, p0, p1))
+
+    def prepare_writes(self, seqs, p0s, counts):
+        """Host int32 arrays; returns the ops int32 numpy array [n, 3] =
+        (block to copy or -1, new block, table entry index), one per table
+        entry the writes change, for cow_apply."""
+        import numpy as np
+
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        p0s = np.ascontiguousarray(p0s, dtype=np.int32)
+        counts = np.ascontiguousarray(counts, dtype=np.int32)
+        n = len(seqs)
+        if len(p0s) != n or len(counts) != n:
+            raise ValueError("seqs, p0s and counts must have equal lengths")
+        # a write of c tokens touches at most c // bs + 2 logical blocks
+        cap = 2 * n + int(counts.sum(dtype=np.int64)) // self.block_size + 1 if n else 1
+        cap = max(cap, 1)
+        if getattr(self, "_ops", None) is None or self._ops.shape[0] < cap:
+            self._ops = np.zeros((cap, 3), dtype=np.int32)
+            self._nc = ctypes.c_int32(0)
+        _check(lib().pkv_pool_prepare_writes(self._h, n, seqs.ctypes.data, p0s.ctypes.data, counts.ctypes.data,
+                                             self._ops.ctypes.data, cap, ctypes.byref(self._nc)))
+        return self._ops[: self._nc.value].copy()
+
+    def export(self):
+        """(table int32 [n_seqs, max_blocks], lengths int32 [n_seqs]) on the host."""
+        import numpy as np
+
+        table = np.zeros((self.n_seqs, self.max_blocks), dtype=np.int32)
+        lens = np.zeros(self.n_seqs, dtype=np.int32)
+        _check(lib().pkv_pool_export(self._h, table.ctypes.data, lens.ctypes.data))
+        return table, lens
+
+
+def cow_apply(k_pool, v_pool, ops, table=None):
+    """Apply BlockPool.prepare_writes ops on the device: copy each op's
+    source block (if any) to its new block in both pools and, if a device
+    table is given (int32 [n_seqs, max_blocks]), patch its entries.  ops is
+    a device int32 tensor [n, 3] or a host array (uploaded first)."""
+    torch = _torch()
+    if not isinstance(ops, torch.Tensor):
+        import numpy as np
+
+        ops = torch.from_numpy(np.ascontiguousarray(ops, dtype=np.int32).reshape(-1, 3)).to(k_pool.device)
+    _i32(ops, "ops")
+    for t in (k_pool, v_pool):
+        if t is not None and not t.is_contiguous():
+            raise TypeError("pools must be contiguous")
+    if table is not None:
+        _i32(table, "table")
+    nb = k_pool.shape[0]
+    if v_pool is not None and v_pool.shape[0] != nb:
+        raise ValueError("K and V pools must have the same number of blocks")
+    kb = k_pool[0].numel() * k_pool.element_size()
+    vb = v_pool[0].numel() * v_pool.element_size() if v_pool is not None else 0
+    _check(lib().pkv_cow_apply(_ptr(k_pool), _ptr(v_pool), nb, kb, vb, _ptr(ops), ops.shape[0], _ptr(table),
+                               table.numel() if table is not None else 0, _stream(k_pool)))
     return k_pool, v_pool

@@ -58,4 +58,62 @@ hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stag
   return hipGetLastError();
 }
 
+// Copy-on-write ops: grid (op, pool, chunk); workgroup (i, k, c) copies
+// chunk c (kCowChunk bytes) of op i's source block in pool k (a block is
+// contiguous in the pool layout), and workgroup (i, 0, 0) also patches the
+// device table entry of op i.  Chunks spread one block over several
+// workgroups: a batch of a few hundred copies then still fills the chip.
+// An op whose source or destination lies outside [0, n_blocks), or whose
+// source equals its destination, copies nothing; an entry outside the
+// table is not patched.  Sources and destinations of one launch are
+// disjoint (the pool hands out fresh destinations), so workgroups never
+// race.
+constexpr int64_t kCowChunk = 8192;
+
+template <typename W>
+__global__ __launch_bounds__(256) void cow_apply_kernel(CowArgs a) {
+  constexpr int kUnroll = 2;
+  const int32_t src = a.ops[3 * blockIdx.x], dst = a.ops[3 * blockIdx.x + 1];
+  const int32_t entry = a.ops[3 * blockIdx.x + 2];
+  if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0 && a.table && entry >= 0 &&
+      entry < a.table_entries)
+    a.table[entry] = dst;
+  if (src < 0 || dst < 0 || src >= a.n_blocks || dst >= a.n_blocks || src == dst) return;
+  unsigned char* base = a.pool[blockIdx.y];
+  if (!base) return;
+  const int64_t bytes = a.block_bytes[blockIdx.y];
+  const int64_t lo = (int64_t)blockIdx.z * kCowChunk;
+  if (lo >= bytes) return;
+  const int64_t words = (bytes < lo + kCowChunk ? bytes - lo : kCowChunk) / (int64_t)sizeof(W);
+  const W* from = (const W*)(base + (int64_t)src * bytes + lo);
+  W* to = (W*)(base + (int64_t)dst * bytes + lo);
+  for (int64_t w0 = threadIdx.x; w0 < words; w0 += (int64_t)kUnroll * blockDim.x) {
+    W v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t w = w0 + (int64_t)u * blockDim.x;
+      if (w < words) v[u] = from[w];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t w = w0 + (int64_t)u * blockDim.x;
+      if (w < words) to[w] = v[u];
+    }
+  }
+}
+
+hipError_t launch_cow_apply(const CowArgs& a, hipStream_t st) {
+  if (a.n_ops <= 0) return hipSuccess;
+  const bool wide = (a.block_bytes[0] % 16) == 0 && (!a.pool[1] || (a.block_bytes[1] % 16) == 0);
+  const int64_t most = a.block_bytes[0] > a.block_bytes[1] ? a.block_bytes[0] : a.block_bytes[1];
+  const int64_t chunks = (most + kCowChunk - 1) / kCowChunk;
+  if (chunks > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)a.n_ops, 2, (unsigned)chunks);
+  if (wide)
+    hipLaunchKernelGGL(cow_apply_kernel<uint4>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(cow_apply_kernel<uint32_t>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -291,6 +291,11 @@ std::vector<int32_t> order_moves_impl(const int32_t* mv, int32_t n) {
 
 }  // namespace
 
+namespace pkv_host {
+// Error message shared with the pool calls (pool.cpp).
+void set_error(const char* msg) { g_err = msg; }
+}  // namespace pkv_host
+
 extern "C" {
 
 int64_t pkv_row_bytes(int32_t fmt, int32_t n_kv_heads, int32_t head_dim) {
@@ -621,6 +626,35 @@ pkv_status pkv_kv_store(const pkv_shape* sh, int32_t n_tok, int32_t src_fmt, con
   hipError_t e = pkv::launch_store(a, src_fmt, hd, (hipStream_t)stream, &found);
   if (!found) return fail(PKV_E_UNSUPPORTED, "no store kernel for head_dim %d", hd);
   if (e != hipSuccess) return device_fail(e, "store launch");
+  return ok();
+}
+
+pkv_status pkv_cow_apply(void* k_pool, void* v_pool, int32_t n_pool_blocks, int64_t k_block_bytes,
+                         int64_t v_block_bytes, const int32_t* ops, int32_t n, int32_t* table,
+                         int64_t table_entries, void* stream) {
+  if (n < 0) return fail(PKV_E_ARG, "negative op count %d", n);
+  if (n == 0) return ok();
+  if (!k_pool || !ops) return fail(PKV_E_ARG, "k_pool and ops must be non-NULL");
+  if (n_pool_blocks <= 0) return fail(PKV_E_ARG, "n_pool_blocks %d must be positive", n_pool_blocks);
+  if (k_block_bytes <= 0 || k_block_bytes % 4 || (v_pool && (v_block_bytes <= 0 || v_block_bytes % 4)))
+    return fail(PKV_E_ARG, "block bytes must be positive multiples of 4");
+  if (table && table_entries < 0) return fail(PKV_E_ARG, "negative table size");
+  if (k_block_bytes > ((int64_t)65535 << 13) || v_block_bytes > ((int64_t)65535 << 13))
+    return fail(PKV_E_ARG, "blocks larger than 512 MiB are not supported");
+  for (const void* p : {(const void*)k_pool, (const void*)v_pool})
+    if (((uintptr_t)p) % 16) return fail(PKV_E_ARG, "pools must be 16-byte aligned");
+  pkv::CowArgs a{};
+  a.pool[0] = (unsigned char*)k_pool;
+  a.pool[1] = (unsigned char*)v_pool;
+  a.block_bytes[0] = k_block_bytes;
+  a.block_bytes[1] = v_pool ? v_block_bytes : 0;
+  a.ops = ops;
+  a.table = table;
+  a.table_entries = table ? table_entries : 0;
+  a.n_ops = n;
+  a.n_blocks = n_pool_blocks;
+  hipError_t e = pkv::launch_cow_apply(a, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "cow_apply launch");
   return ok();
 }
 

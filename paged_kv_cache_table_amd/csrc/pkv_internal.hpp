@@ -223,4 +223,17 @@ struct StoreArgs {
 // Grid: ceil(n_tok * n_kv_heads / units per workgroup) x 256 threads.
 hipError_t launch_store(const StoreArgs& a, int src_fmt, int hd, hipStream_t st, bool* found);
 
+// Copy-on-write ops: copy block src (if >= 0) to dst in both pools and set
+// table[entry] = dst (pool[1] and table may be null).
+struct CowArgs {
+  unsigned char* pool[2];
+  int64_t block_bytes[2];  // bytes of one block of each pool (a multiple of 4)
+  const int32_t* ops;      // [n_ops][3] = (src or -1, dst, table entry)
+  int32_t* table;          // device block tables, table_entries int32
+  int64_t table_entries;
+  int32_t n_ops, n_blocks;
+};
+// Grid (n_ops, 2, ceil(largest block bytes / 8 KiB)) x 256 threads.
+hipError_t launch_cow_apply(const CowArgs& a, hipStream_t st);
+
 }  // namespace pkv
