@@ -18,7 +18,7 @@ resident in HBM.  Prints one JSON line:
   workload on this host.
 
 Other workloads (for the record; the default is the headline): decode1,
-decode2, decode5, prefill4, copy5b, store4, cow3; and calib, a plain device copy of known
+decode2, decode5, prefill4, copy5b, store4, cow3, defrag3; and calib, a plain device copy of known
 size used to scale the HBM byte counters.
 
 Counter summary (turns two rocprofv3 --pmc runs, FETCH_SIZE then WRITE_SIZE,
@@ -615,13 +615,80 @@ def run_cow(args):
     }
 
 
+def run_defrag(args):
+    """Compaction of a fragmented pool: 64 sequences of 4096..32768 tokens
+    (7B-class layer: 8 kv heads, hd 128, block 16, f16 K/V) allocated
+    through the block pool, then every other one dropped; defrag(-1) moves
+    the live blocks above the live count into the holes below and the row
+    moves run through kv_copy_cells.  Timed per step by wall clock: the
+    pool's plan, copy_cells' plan and upload, and the device copies."""
+    import torch
+
+    import paged_kv_cache_table_amd as pkv
+
+    rng = np.random.default_rng(3)
+    n_seqs, hkv, hd, bs = 64, 8, 128, 16
+    L = rng.integers(4096, 32769, size=n_seqs).astype(np.int32)
+    max_blocks = 32768 // bs
+    n_blocks = int(np.sum((L + bs - 1) // bs)) + 1024
+    log(f"[bench] defrag: {n_seqs} sequences, {n_blocks} blocks per pool")
+    k = torch.empty((n_blocks, hkv, bs, hd), dtype=torch.float16, device="cuda")
+    v = torch.empty_like(k)
+
+    def fragmented():
+        pool = pkv.BlockPool(n_blocks, n_seqs, max_blocks, bs)
+        for s_ in range(n_seqs):
+            pool.prepare_writes([s_], [0], [int(L[s_])])
+        for s_ in range(0, n_seqs, 2):
+            pool.remove(s_, 0, 1 << 30)
+        return pool
+
+    row_bytes = 2 * hkv * hd * 2  # K and V rows
+    walls, plans, devs = [], [], []
+    moved_rows = 0
+    for it in range(args.warmup + args.steps):
+        pool = fragmented()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        moves = pool.defrag(-1)
+        t1 = time.perf_counter()
+        e0.record()
+        pkv.kv_copy_cells(k, v, moves)
+        e1.record()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        if it >= args.warmup:
+            walls.append(t2 - t0)
+            plans.append(t1 - t0)
+            devs.append(e0.elapsed_time(e1))
+        moved_rows = int(moves[:, 2].sum())
+    wall = float(np.mean(walls))
+    dev_ms = float(np.mean(devs))
+    moved_bytes = 2 * moved_rows * row_bytes  # each moved row read once and written once
+    gbs = moved_bytes / (dev_ms * 1e-3) / 1e9
+    return {
+        "metric": "defrag: rows moved per second (pool plan + copy_cells plan, upload and copies)",
+        "value": round(moved_rows / wall, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bytes", "data": "synthetic",
+        "config": {"workload": f"{n_seqs} sequences of 4096..32768 tokens (8 kv heads, hd 128, block 16, f16 K/V), "
+                               "every other one dropped, then defrag(-1) + kv_copy_cells; wall clock",
+                   "moves": int(len(moves)), "moved_rows": moved_rows, "moved_bytes": moved_bytes},
+        "pool_plan_ms": round(float(np.mean(plans)) * 1e3, 4),
+        "roofline": {"bound": "hbm", "kernel": "copy_rows_kernel (copy_cells: plan upload + copies)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "device_ms": round(dev_ms, 5)},
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode3",
-                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "cow3", "calib"])
+                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "cow3", "defrag3", "calib"])
     ap.add_argument("--pmc-summary", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
     ap.add_argument("--split", type=int, default=0, help="decode split size in tokens (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -655,6 +722,8 @@ def main(argv=None):
         res = run_store(args)
     elif args.workload == "cow3":
         res = run_cow(args)
+    elif args.workload == "defrag3":
+        res = run_defrag(args)
     elif args.workload == "copy5b":
         res = run_copy(args)
     else:

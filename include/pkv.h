@@ -337,6 +337,25 @@ pkv_status pkv_pool_prepare_writes(pkv_block_pool* pool, int32_t n, const int32_
                                    const int32_t* p0s, const int32_t* counts, int32_t* ops_out,
                                    int32_t max_ops, int32_t* n_ops);
 
+/* Compaction ("KV Cache Design", section 2: a compaction changes only cells,
+ * so rows move verbatim through copy_cells in order_moves order, and the
+ * defragmenter returns the moves for whoever caches block ids).  Makes the
+ * top `need` block ids free (need < 0: as many as are free, so every live
+ * block ends below the live count): the live blocks among them, ascending,
+ * move into the lowest free blocks, ascending; tables and reference counts
+ * follow at once.  A block-table sequence need not be contiguous, so holes
+ * are filled instead of sliding everything down: the fewest blocks move and
+ * every move goes down onto a free row (no destination is a source).
+ * moves_out: host int32 [max_moves][3] (src_row, dst_row, len) in pool rows
+ * (row = block * block_size + slot), consecutive blocks that land on
+ * consecutive blocks merged; apply them to the K and V pools with
+ * pkv_kv_copy_cells, and re-export the tables, before the next read.
+ * PKV_E_CAPACITY if need exceeds the free blocks, PKV_E_WORKSPACE if
+ * max_moves is too small (at most one move per moved block); a refused call
+ * changes nothing. */
+pkv_status pkv_pool_defrag(pkv_block_pool* pool, int32_t need, int32_t* moves_out, int32_t max_moves,
+                           int32_t* n_moves);
+
 /* Host copies of the tables (int32 [n_seqs][max_blocks_per_seq]) and, if
  * lens_out is not NULL, the lengths (int32 [n_seqs]). */
 pkv_status pkv_pool_export(const pkv_block_pool* pool, int32_t* table_out, int32_t* lens_out);

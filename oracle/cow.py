@@ -39,6 +39,21 @@ Readings where the pages are silent:
 * a prepare that needs more fresh blocks than are free is refused and
   changes nothing; the watermark only affects can_allocate (admission):
   free - n >= watermark.
+
+Compaction ("KV Cache Design", section 2: a compaction changes only cells,
+so rows move verbatim through copy_cells in order_moves order; the
+defragmenter returns the moves and whoever caches block ids applies them):
+* defrag(need) makes the top `need` blocks of the pool free (need < 0: all
+  free blocks, i.e. every live block ends below the number of live
+  blocks).  The live blocks found in that top range, in ascending id order,
+  move into the lowest free blocks below it, in ascending order; every
+  table entry follows its block and reference counts move along.  In a
+  block-table pool a sequence's blocks need not be contiguous, so holes are
+  filled rather than everything slid down: the fewest blocks move, and no
+  destination is ever a source (every move goes down, onto a free row).
+  Moves are pool rows (src_row, dst_row, len), consecutive blocks that land
+  on consecutive blocks merged into one move; need larger than the free
+  blocks is refused and changes nothing.
 """
 
 from __future__ import annotations
@@ -157,6 +172,38 @@ class BlockPoolModel:
                     self.table[s, lb] = nb
             self.length[s] = max(self.length[s], p0 + n)
         return copies
+
+    def defrag(self, need: int):
+        """Returns the row moves [(src_row, dst_row, len)] and applies the
+        block relocation to the tables, counts and free set."""
+        nf = self.n_free()
+        if need < 0:
+            need = nf
+        if need > nf:
+            raise ValueError("fewer free blocks than needed")
+        top = self.n_blocks - need
+        srcs = [b for b in range(top, self.n_blocks) if self.ref[b] > 0]
+        holes = [b for b in range(top) if self.ref[b] == 0][: len(srcs)]
+        assert len(holes) == len(srcs)
+        where = {}
+        for s, d in zip(srcs, holes):
+            where[s] = d
+        for q in range(self.n_seqs):
+            for lb in range(self.max_blocks):
+                b = int(self.table[q, lb])
+                if b in where:
+                    self.table[q, lb] = where[b]
+        for s, d in zip(srcs, holes):
+            self.ref[d], self.ref[s] = self.ref[s], 0
+        self._free = [b for b in range(self.n_blocks) if self.ref[b] == 0]
+        heapq.heapify(self._free)
+        moves = []
+        for s, d in zip(srcs, holes):
+            if moves and moves[-1][0] + moves[-1][2] == s * self.bs and moves[-1][1] + moves[-1][2] == d * self.bs:
+                moves[-1][2] += self.bs
+            else:
+                moves.append([s * self.bs, d * self.bs, self.bs])
+        return [tuple(m) for m in moves]
 
     # -- checks ---------------------------------------------------------------
     def check(self):

@@ -53,6 +53,7 @@ EXPORTS = (
     "pkv_pool_fork",
     "pkv_pool_remove",
     "pkv_pool_prepare_writes",
+    "pkv_pool_defrag",
     "pkv_pool_export",
     "pkv_cow_apply",
     "pkv_resolve_rows",
@@ -121,6 +122,7 @@ def lib() -> ctypes.CDLL:
         "pkv_pool_fork": (I32, [P, I32, I32, I32]),
         "pkv_pool_remove": (I32, [P, I32, I32, I32]),
         "pkv_pool_prepare_writes": (I32, [P, I32, P, P, P, P, I32, P]),
+        "pkv_pool_defrag": (I32, [P, I32, P, I32, P]),
         "pkv_pool_export": (I32, [P, P, P]),
         "pkv_cow_apply": (I32, [P, P, I32, I64, I64, P, I32, P, I64, P]),
         "pkv_resolve_rows": (I32, [SH, I32, P, P, P, P, I32, I32, P, I32, P, P]),
@@ -491,6 +493,19 @@ class BlockPool:
         _check(lib().pkv_pool_prepare_writes(self._h, n, seqs.ctypes.data, p0s.ctypes.data, counts.ctypes.data,
                                              self._ops.ctypes.data, cap, ctypes.byref(self._nc)))
         return self._ops[: self._nc.value].copy()
+
+    def defrag(self, need: int = -1):
+        """Free the top `need` block ids (need < 0: every free block) by
+        moving the live blocks there into the lowest free blocks; returns
+        the row moves int32 [n, 3] (src_row, dst_row, len) for kv_copy_cells.
+        The pool's tables already follow; re-export them to the device."""
+        import numpy as np
+
+        cap = max(1, self.n_blocks - self.free_blocks())
+        out = np.zeros((cap, 3), dtype=np.int32)
+        nm = ctypes.c_int32(0)
+        _check(lib().pkv_pool_defrag(self._h, need, out.ctypes.data, cap, ctypes.byref(nm)))
+        return out[: nm.value].copy()
 
     def export(self):
         """(table int32 [n_seqs, max_blocks], lengths int32 [n_seqs]) on the host."""

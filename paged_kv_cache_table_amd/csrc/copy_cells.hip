@@ -42,6 +42,82 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(int phase, PoolGeom g, u
   }
 }
 
+// Disjoint runs: when no move's destination touches any move's source and
+// destinations do not overlap, every order gives the same bytes, so all rows
+// copy at once straight from the moves.  Workgroup b takes global rows
+// [16b, 16b + 16) of the concatenated moves (cum = prefix sums of the move
+// lengths) and copies each row's n_kv_heads segments.
+template <typename W>
+__global__ __launch_bounds__(256) void copy_runs_kernel(PoolGeom g, const int32_t* moves,
+                                                        const int32_t* cum, int32_t n_moves,
+                                                        int32_t total_rows) {
+  constexpr int kRows = 16, kUnroll = 4;
+  __shared__ int64_t src_off[kRows], dst_off[kRows];  // byte offset of the row's first segment
+  const int64_t head_stride = g.block_size * g.seg_bytes;
+  const int64_t block_bytes = g.n_kv_heads * head_stride;
+  const int32_t r0 = (int32_t)blockIdx.x * kRows;
+  if (threadIdx.x < kRows) {
+    const int32_t r = r0 + (int32_t)threadIdx.x;
+    int64_t so = -1, dof = -1;
+    if (r < total_rows) {
+      int32_t lo = 0, hi = n_moves - 1;  // last move with cum[m] <= r
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (cum[mid] <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      const int64_t o = r - cum[lo];
+      const int64_t sr = moves[3 * lo] + o, dr = moves[3 * lo + 1] + o;
+      so = (sr / g.block_size) * block_bytes + (sr % g.block_size) * g.seg_bytes;
+      dof = (dr / g.block_size) * block_bytes + (dr % g.block_size) * g.seg_bytes;
+    }
+    src_off[threadIdx.x] = so;
+    dst_off[threadIdx.x] = dof;
+  }
+  __syncthreads();
+  const uint32_t per_seg = (uint32_t)(g.seg_bytes / (int64_t)sizeof(W));
+  const uint32_t per_row = per_seg * (uint32_t)g.n_kv_heads;
+  const uint32_t total = kRows * per_row;
+  // word f of the workgroup: row f / per_row, head h, word c of the segment
+  auto at = [&](int64_t row_off, uint32_t w) {
+    const uint32_t h = w / per_seg, c = w - h * per_seg;
+    return (W*)(g.base + row_off + h * head_stride) + c;
+  };
+  for (uint32_t f0 = threadIdx.x; f0 < total; f0 += kUnroll * blockDim.x) {
+    W v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t f = f0 + u * blockDim.x;
+      if (f < total) {
+        const uint32_t i = f / per_row;
+        if (src_off[i] >= 0) v[u] = *at(src_off[i], f - i * per_row);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t f = f0 + u * blockDim.x;
+      if (f < total) {
+        const uint32_t i = f / per_row;
+        if (dst_off[i] >= 0) *at(dst_off[i], f - i * per_row) = v[u];
+      }
+    }
+  }
+}
+
+hipError_t launch_copy_runs(const PoolGeom& pool, const int32_t* moves, const int32_t* cum,
+                            int32_t n_moves, int32_t total_rows, hipStream_t st) {
+  if (n_moves <= 0 || total_rows <= 0) return hipSuccess;
+  const bool wide = (pool.seg_bytes % 16) == 0;
+  const unsigned blocks = (unsigned)((total_rows + 15) / 16);
+  if (wide)
+    hipLaunchKernelGGL(copy_runs_kernel<uint4>, dim3(blocks), dim3(256), 0, st, pool, moves, cum, n_moves,
+                       total_rows);
+  else
+    hipLaunchKernelGGL(copy_runs_kernel<uint32_t>, dim3(blocks), dim3(256), 0, st, pool, moves, cum,
+                       n_moves, total_rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stage,
                             const int32_t* pairs, int32_t n_pairs, hipStream_t st) {
   if (n_pairs <= 0) return hipSuccess;

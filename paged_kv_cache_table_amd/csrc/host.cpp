@@ -289,6 +289,33 @@ std::vector<int32_t> order_moves_impl(const int32_t* mv, int32_t n) {
   return up;
 }
 
+// The effective moves (len > 0, src != dst) as (src, dst, len), and whether
+// they are disjoint: destinations do not overlap each other and no
+// destination overlaps any source.  Then every application order gives the
+// same bytes and all rows can be copied at once.
+bool disjoint_moves(const int32_t* mv, int32_t n, std::vector<int32_t>* eff) {
+  eff->clear();
+  std::vector<std::pair<int64_t, int64_t>> src, dst;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t s = mv[3 * i], d = mv[3 * i + 1], len = mv[3 * i + 2];
+    if (len <= 0 || s == d) continue;
+    eff->insert(eff->end(), {(int32_t)s, (int32_t)d, (int32_t)len});
+    src.push_back({s, s + len});
+    dst.push_back({d, d + len});
+  }
+  std::sort(src.begin(), src.end());
+  std::sort(dst.begin(), dst.end());
+  for (size_t i = 1; i < dst.size(); ++i)
+    if (dst[i].first < dst[i - 1].second) return false;
+  size_t j = 0;  // sweep: sources ending after the current destination's start
+  for (const auto& d : dst) {
+    while (j < src.size() && src[j].second <= d.first) ++j;
+    for (size_t k = j; k < src.size() && src[k].first < d.second; ++k)
+      if (src[k].second > d.first) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 namespace pkv_host {
@@ -429,6 +456,9 @@ pkv_status pkv_order_moves(const int32_t* moves, int32_t n, int32_t* order_out, 
 size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t row_bytes_k,
                                       int64_t row_bytes_v) {
   if (n < 0 || (n > 0 && !moves) || row_bytes_k <= 0 || row_bytes_v < 0) return 0;
+  std::vector<int32_t> eff;
+  if (disjoint_moves(moves, n, &eff))  // moves and their prefix sums only
+    return align_up((eff.size() + eff.size() / 3 + 1) * sizeof(int32_t), 256) + 256;
   int64_t rows = 0;
   for (int32_t i = 0; i < n; ++i)
     if (moves[3 * i + 2] > 0 && moves[3 * i] != moves[3 * i + 1]) rows += moves[3 * i + 2];
@@ -466,6 +496,35 @@ pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, 
   }
   const std::vector<int32_t> order = order_moves_impl(moves, n);
   if (order.empty()) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  std::vector<int32_t> eff;
+  if (disjoint_moves(moves, n, &eff)) {
+    // No destination touches a source: copy every run at once.
+    const int32_t m = (int32_t)(eff.size() / 3);
+    std::vector<int32_t> up(eff);
+    int64_t total = 0;
+    up.push_back(0);
+    for (int32_t i = 0; i < m; ++i) {
+      total += eff[3 * i + 2];
+      up.push_back((int32_t)total);  // cum[i + 1]; total <= pool rows < 2^31
+    }
+    const size_t need = align_up(up.size() * sizeof(int32_t), 256) + 256;
+    if (!ws || ws_bytes < need)
+      return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  ws ? ws_bytes : (size_t)0, need);
+    hipError_t e = hipMemcpyAsync(ws, up.data(), up.size() * sizeof(int32_t), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return device_fail(e, "uploading the moves");
+    const int32_t* d_moves = (const int32_t*)ws;
+    const int32_t* d_cum = d_moves + eff.size();
+    for (const pkv::PoolGeom g : {pkv::PoolGeom{(unsigned char*)k_pool, seg_bytes_k, n_kv_heads, block_size},
+                                  pkv::PoolGeom{(unsigned char*)v_pool, seg_bytes_v, n_kv_heads, block_size}}) {
+      if (!g.base) continue;
+      e = pkv::launch_copy_runs(g, d_moves, d_cum, m, (int32_t)total, st);
+      if (e != hipSuccess) return device_fail(e, "copy_cells run launch");
+    }
+    return ok();
+  }
   // Final source of every row of [lo, hi) after the ordered memmoves.
   std::vector<int32_t> prov(hi - lo);
   for (int64_t r = lo; r < hi; ++r) prov[r - lo] = (int32_t)r;
@@ -509,7 +568,6 @@ pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, 
   if (!ws || ws_bytes < need)
     return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 ws ? ws_bytes : (size_t)0, need);
-  hipStream_t st = (hipStream_t)stream;
   std::vector<int32_t> idx(gather);
   idx.insert(idx.end(), scatter.begin(), scatter.end());
   int32_t* d_idx = (int32_t*)ws;

@@ -207,6 +207,11 @@ struct PoolGeom {
 };
 hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stage,
                             const int32_t* pairs, int32_t n_pairs, hipStream_t st);
+// Disjoint row moves (no destination touches a source): moves [n][3] and
+// cum [n + 1] (prefix sums of the lengths) on the device; grid
+// ceil(total_rows / 16) x 256 threads.
+hipError_t launch_copy_runs(const PoolGeom& pool, const int32_t* moves, const int32_t* cum,
+                            int32_t n_moves, int32_t total_rows, hipStream_t st);
 hipError_t launch_zero_words(int32_t* p, int n, hipStream_t st);
 
 // Store of new K/V rows through the block table (pool[1] may be null).

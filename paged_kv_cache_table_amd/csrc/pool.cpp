@@ -25,7 +25,12 @@
 //    block; the length becomes max(len, p0 + n).  Checked in full before
 //    any change.  Every table entry it changes is reported as an op
 //    (source block or -1, fresh block, entry index) for the device, which
-//    copies the source block (if any) and patches its copy of the table.
+//    copies the source block (if any) and patches its copy of the table;
+//  - defrag(need): the live blocks in the top `need` ids, ascending, move
+//    into the lowest free blocks, ascending (need < 0: every free block);
+//    tables and counts follow; the row moves (consecutive blocks landing on
+//    consecutive blocks merged) go to copy_cells.  Every move goes down
+//    onto a free row, so no destination is ever a source.
 //
 // The free set is a two-level bitmap (one bit per block, one bit per 64-bit
 // word), so the smallest free id is found in a few word scans.
@@ -82,6 +87,12 @@ struct pkv_block_pool {
   }
   void release(int32_t b) {
     if (--ref[b] == 0) mark_free(b);
+  }
+  bool is_free(int32_t b) const { return (l0[b >> 6] >> (b & 63)) & 1; }
+  void take(int32_t b) {  // a specific free block
+    l0[b >> 6] &= ~(1ull << (b & 63));
+    if (!l0[b >> 6]) l1[b >> 12] &= ~(1ull << ((b >> 6) & 63));
+    --n_free;
   }
   int32_t nblk(int64_t n_tokens) const { return (int32_t)((n_tokens + bs - 1) / bs); }
   void next_gen() {
@@ -147,7 +158,7 @@ pkv_status pkv_pool_create(int32_t n_blocks, int32_t n_seqs, int32_t max_blocks_
   if (n_blocks <= 0 || n_seqs <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 || watermark < 0)
     return perr(PKV_E_ARG, "pool sizes must be positive and the watermark non-negative");
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX ||
-      (int64_t)n_seqs * max_blocks_per_seq > INT32_MAX)
+      (int64_t)n_seqs * max_blocks_per_seq > INT32_MAX || (int64_t)n_blocks * block_size > INT32_MAX)
     return perr(PKV_E_ARG, "pool geometry too large");
   pkv_block_pool* p = new (std::nothrow) pkv_block_pool;
   if (!p) return perr(PKV_E_ARG, "out of host memory");
@@ -298,6 +309,50 @@ pkv_status pkv_pool_prepare_writes(pkv_block_pool* p, int32_t n, const int32_t* 
     p->length[s] = std::max(p->length[s], a + c);
   }
   *n_ops = k;
+  return pok();
+}
+
+pkv_status pkv_pool_defrag(pkv_block_pool* p, int32_t need, int32_t* moves_out, int32_t max_moves,
+                           int32_t* n_moves) {
+  if (!p || !n_moves) return perr(PKV_E_ARG, "pool or n_moves is NULL");
+  *n_moves = 0;
+  if (need < 0) need = p->n_free;
+  if (need > p->n_free) return perr(PKV_E_CAPACITY, "fewer free blocks than the defrag needs");
+  const int32_t top = p->n_blocks - need;
+  std::vector<int32_t> srcs, holes;
+  for (int32_t b = top; b < p->n_blocks; ++b)
+    if (p->ref[b] > 0) srcs.push_back(b);
+  for (int32_t b = 0; b < top && holes.size() < srcs.size(); ++b)
+    if (p->ref[b] == 0) holes.push_back(b);
+  // Count the merged row moves before changing anything.
+  int32_t nm = 0;
+  for (size_t i = 0; i < srcs.size(); ++i)
+    if (i == 0 || srcs[i] != srcs[i - 1] + 1 || holes[i] != holes[i - 1] + 1) ++nm;
+  if (nm > 0 && (!moves_out || nm > max_moves))
+    return perr(PKV_E_WORKSPACE, "moves_out is too small for the moves this defrag makes");
+  if (srcs.empty()) return pok();
+  std::vector<int32_t> where(p->n_blocks - top, -1);
+  for (size_t i = 0; i < srcs.size(); ++i) where[srcs[i] - top] = holes[i];
+  for (int32_t& e : p->table)
+    if (e >= top) e = where[e - top];
+  int32_t k = -1;
+  const int64_t bs = p->bs;
+  for (size_t i = 0; i < srcs.size(); ++i) {
+    const int32_t a = srcs[i], d = holes[i];
+    p->ref[d] = p->ref[a];
+    p->ref[a] = 0;
+    p->take(d);
+    p->mark_free(a);
+    if (i > 0 && a == srcs[i - 1] + 1 && d == holes[i - 1] + 1) {
+      moves_out[3 * k + 2] += (int32_t)bs;
+    } else {
+      ++k;
+      moves_out[3 * k] = (int32_t)(a * bs);
+      moves_out[3 * k + 1] = (int32_t)(d * bs);
+      moves_out[3 * k + 2] = (int32_t)bs;
+    }
+  }
+  *n_moves = k + 1;
   return pok();
 }
 

@@ -165,3 +165,16 @@ def test_resolve_refusals():
     assert st == 1 and "n_q_total == n_seqs" in pkv.last_error()
     st = L.pkv_resolve_rows(ctypes.byref(sh), 2, FAKE, None, FAKE, FAKE, 0, 1, None, 10, FAKE, None)
     assert st == 1
+
+
+def test_copy_cells_workspace_for_disjoint_moves_is_small():
+    """Moves whose destinations touch no source need no stage: the workspace
+    holds only the moves and their prefix sums."""
+    import ctypes
+
+    mv = np.array([[0, 100, 10], [200, 20, 30], [50, 300, 5]], dtype=np.int32)
+    small = pkv.lib().pkv_copy_cells_workspace_bytes(mv.ctypes.data, 3, 4096, 4096)
+    assert small <= 512
+    overlapping = np.array([[0, 5, 10], [200, 20, 30]], dtype=np.int32)  # 0..9 -> 5..14 overlaps itself
+    big = pkv.lib().pkv_copy_cells_workspace_bytes(overlapping.ctypes.data, 2, 4096, 4096)
+    assert big >= 40 * 4096

@@ -136,3 +136,44 @@ def test_full_size_10k_overlapping_moves():
     log(f"  {changed} rows changed")
     _check(k, prov, 1)
     _check(v, prov, 2)
+
+
+def _disjoint_moves(rng, n_moves, n_rows, max_len):
+    """Random moves whose destinations overlap neither each other nor any
+    source: 2 * n_moves disjoint intervals, each length used twice, each
+    pair split into a source and a destination in random direction."""
+    lens = rng.integers(1, max_len + 1, size=n_moves)
+    slots = rng.permutation(np.repeat(np.arange(n_moves), 2))
+    gaps = rng.integers(0, 3, size=2 * n_moves)
+    assert int(lens.sum()) * 2 + int(gaps.sum()) <= n_rows
+    starts, pos = {}, 0
+    for k, m in enumerate(slots):
+        pos += int(gaps[k])
+        starts.setdefault(int(m), []).append(pos)
+        pos += int(lens[m])
+    moves = []
+    for m in range(n_moves):
+        a, b = starts[m]
+        if rng.random() < 0.5:
+            a, b = b, a
+        moves.append((a, b, int(lens[m])))
+    return np.array(moves, dtype=np.int32)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_disjoint_moves_bit_exact(seed):
+    """Move sets where no destination touches a source take the one-pass
+    run copy; bytes must equal the oracle's sequential memmoves."""
+    rng = np.random.default_rng(300 + seed)
+    blocks, bs = 64, [16, 7, 32, 1][seed]
+    n_rows = blocks * bs
+    kh = _rand_pool(rng, blocks, 3, bs, [512, 68, 136, 36][seed], "u8")
+    vh = _rand_pool(rng, blocks, 3, bs, 256, "float16")
+    max_len = max(1, min(32, n_rows // 64))
+    moves = _disjoint_moves(rng, max(4, n_rows // (4 * max_len + 8)), n_rows, max_len)
+    k, v = kh.cuda(), vh.cuda()
+    ref = [kh.numpy().copy(), vh.numpy().copy()]
+    oracle.copy_cells(ref, moves)
+    pkv.kv_copy_cells(k, v, moves)
+    assert np.array_equal(k.cpu().numpy().view(np.uint8), ref[0].view(np.uint8))
+    assert np.array_equal(v.cpu().numpy().view(np.uint8), ref[1].view(np.uint8))

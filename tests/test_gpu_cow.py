@@ -181,3 +181,43 @@ def test_remove_then_rewrite_through_the_pool():
     b.sync_table()
     b.write([1, 2, 0], [30, 9, 4])
     b.check()
+
+
+@pytest.mark.parametrize("bs,need_kind", [(16, "full"), (16, "part"), (32, "full")])
+def test_defrag_moves_rows_and_attention_is_bitwise_unchanged(bs, need_kind):
+    """Fragment the pool (writes, forks, dropped sequences), then compact:
+    the library's moves equal the oracle's, the pools after kv_copy_cells
+    equal the oracle's sequential copy_cells bit for bit, and decode over
+    every sequence gives bitwise the same result as before the compaction."""
+    import torch
+
+    rng = np.random.default_rng(70 + bs)
+    hkv, hd, hq = 8, 128, 32
+    n_seqs, max_blocks = 12, 600 // bs + 2
+    b = Both(rng, n_seqs * max_blocks, n_seqs, max_blocks, bs, hkv, hd)
+    for s in range(0, n_seqs, 3):
+        b.write([s], [int(rng.integers(50, 400))])
+        for d in (s + 1, s + 2):
+            b.fork(s, d, int(b.mp.length[s]) // 2)
+            b.write([d], [int(rng.integers(1, 120))])
+    for s in (0, 4, 5, 9):
+        b.lp.remove(s, 0, 1 << 30)
+        b.mp.remove(s, 0, 1 << 30)
+    b.lp.remove(7, 40, 90)  # a middle removal: holes in a live sequence
+    b.mp.remove(7, 40, 90)
+    b.sync_table()
+    b.check()
+    q = torch.randn((n_seqs, hq, hd), generator=torch.Generator().manual_seed(2)).half().cuda()
+    before = b.decode(q, list(range(n_seqs)))
+    # "part": all but a few free blocks, so the top range still holds live blocks
+    need = -1 if need_kind == "full" else b.mp.n_free() - 5
+    moves = b.lp.defrag(need)
+    want = b.mp.defrag(need)
+    assert [tuple(m) for m in moves.tolist()] == want and len(want) > 0
+    pkv.kv_copy_cells(b.k, b.v, moves)
+    oracle.copy_cells([b.kh, b.vh], want)
+    b.sync_table()
+    b.check()
+    after = b.decode(q, list(range(n_seqs)))
+    log(f"  defrag bs {bs} {need_kind}: {len(want)} moves, {sum(m[2] for m in want)} rows")
+    assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])

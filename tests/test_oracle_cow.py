@@ -8,7 +8,12 @@
 * reference-count invariants after every operation;
 * worked scenarios: the number of block copies a fork storm costs, the
   parent keeping its block, refusal leaving the state unchanged, the
-  watermark.
+  watermark;
+* compaction: after defrag and its row moves (applied by the oracle's
+  sequential copy_cells), every sequence reads the same tokens, the top
+  `need` blocks are free, every move goes down onto rows no move reads
+  (so the sequential result equals a simultaneous gather), and only the
+  live blocks of the top range move.
 """
 
 import numpy as np
@@ -216,3 +221,88 @@ def test_fork_refusals():
     m.fork(0, 1, 5)
     with pytest.raises(ValueError):
         m.fork(0, 1)  # destination not empty
+
+
+def _apply_moves_to_blocks(pg, moves):
+    """Row moves on the token-id pool [n_blocks, bs], through the oracle's
+    sequential copy_cells (a pool of rows is [n_rows, 1])."""
+    rows = pg.data.reshape(-1, 1)
+    before = rows.copy()
+    oracle_copy_cells([rows], moves)
+    # simultaneous gather: every destination row takes its source's old value
+    gathered = before.copy()
+    for s_, d_, n_ in moves:
+        gathered[d_ : d_ + n_] = before[s_ : s_ + n_]
+    assert np.array_equal(rows, gathered)
+
+
+from oracle.moves import copy_cells as oracle_copy_cells  # noqa: E402
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_defrag_keeps_every_sequence_and_frees_the_top(seed):
+    rng = np.random.default_rng(50 + seed)
+    bs = [1, 4, 16, 2][seed % 4]
+    n_seqs, max_blocks = 12, 60 // bs + 2
+    n_blocks = n_seqs * max_blocks
+    pg = Paged(n_blocks, n_seqs, max_blocks, bs)
+    nv = Naive(n_seqs, bs)
+    tok = iter(range(10 ** 9))
+    for _ in range(120):  # fragment the pool: writes, forks, removals
+        s = int(rng.integers(0, n_seqs))
+        op = rng.integers(0, 6)
+        L = int(pg.m.length[s])
+        if op < 3:
+            n = int(rng.integers(1, 12))
+            if L + n <= max_blocks * bs:
+                toks = [next(tok) for _ in range(n)]
+                pg.write(([s], [L]), [toks])
+                nv.write(s, L, toks)
+        elif op < 4:
+            empty = [d for d in range(n_seqs) if d != s and pg.m.length[d] == 0]
+            if empty:
+                d = int(rng.choice(empty))
+                n = int(rng.integers(0, L + 1))
+                pg.m.fork(s, d, n)
+                nv.fork(s, d, n)
+        else:
+            p0 = int(rng.integers(0, L + 1))
+            p1 = L if op == 5 else int(rng.integers(p0, L + 1))
+            pg.m.remove(s, p0, p1)
+            nv.remove(s, p0, p1)
+    n_free = pg.m.n_free()
+    need = [-1, n_free, n_free // 2, 0][seed % 4]
+    live_top = int(np.count_nonzero(pg.m.ref[n_blocks - (n_free if need < 0 else need):] > 0))
+    moves = pg.m.defrag(need)
+    # only the live blocks of the top range moved, each down onto a free row
+    assert sum(m[2] for m in moves) == live_top * bs
+    srcs = set()
+    for s_, d_, n_ in moves:
+        assert d_ < s_ and n_ > 0 and n_ % bs == 0
+        srcs.update(range(s_, s_ + n_))
+    for s_, d_, n_ in moves:
+        assert not srcs.intersection(range(d_, d_ + n_))
+    _apply_moves_to_blocks(pg, moves)
+    top = n_blocks - (n_free if need < 0 else need)
+    assert np.all(pg.m.ref[top:] == 0)
+    _agree(pg, nv, n_seqs)
+
+
+def test_defrag_worked_example():
+    """Blocks 0..7, block size 2: live blocks 1, 4, 6 and 7 (7 shared by two
+    sequences); defrag(4) frees 4..7: 4 -> 0, 6 -> 2, 7 -> 3 (6 and 7 land on
+    consecutive blocks: one move of 4 rows)."""
+    m = BlockPoolModel(8, 3, 4, 2)
+    m.table[0, :2] = [1, 7]
+    m.table[1, :3] = [4, 6, 7]
+    m.length[:2] = [4, 6]
+    m.ref[[1, 4, 6, 7]] = [1, 1, 1, 2]
+    m._free = [0, 2, 3, 5]
+    moves = m.defrag(4)
+    assert moves == [(8, 0, 2), (12, 4, 4)]
+    assert m.table[0, :2].tolist() == [1, 3] and m.table[1, :3].tolist() == [0, 2, 3]
+    assert m.ref.tolist() == [1, 1, 1, 2, 0, 0, 0, 0]
+    m.check()
+    with pytest.raises(ValueError):
+        m.defrag(5)
+    assert m.defrag(4) == []

@@ -30,9 +30,9 @@ def test_random_operations_match_the_model(seed):
     n_blocks = int(n_seqs * max_blocks * (0.6 if seed % 2 else 1.2)) + 1  # odd seeds run out of blocks
     lp = pkv.BlockPool(n_blocks, n_seqs, max_blocks, bs, watermark=seed % 3)
     mp = BlockPoolModel(n_blocks, n_seqs, max_blocks, bs, watermark=seed % 3)
-    refusals = copies = 0
+    refusals = copies = moved = 0
     for step in range(400):
-        op = rng.integers(0, 12)
+        op = rng.integers(0, 13)
         s = int(rng.integers(0, n_seqs))
         L = int(mp.length[s])
         if op < 5:
@@ -81,12 +81,25 @@ def test_random_operations_match_the_model(seed):
         elif op < 11:  # drop a whole sequence, which makes room for forks
             mp.remove(s, 0, L)
             lp.remove(s, 0, L)
-        else:
-            n = int(rng.integers(0, n_blocks + 1))
-            assert lp.can_allocate(n) == mp.can_allocate(n)
+        else:  # compaction
+            need = int(rng.integers(-1, mp.n_free() + 2))
+            try:
+                want = mp.defrag(need)
+                err = None
+            except ValueError as e:
+                err = e
+            if err is None:
+                got = lp.defrag(need)
+                assert [tuple(m) for m in got.tolist()] == want
+                moved += sum(m[2] for m in want)
+            else:
+                with pytest.raises(pkv.PkvError):
+                    lp.defrag(need)
+        n = int(rng.integers(0, n_blocks + 1))
+        assert lp.can_allocate(n) == mp.can_allocate(n)
         _same(lp, mp)
         mp.check()
-    assert copies > 0
+    assert copies + moved > 0
     if seed % 2:
         assert refusals > 0
 
@@ -148,3 +161,38 @@ def test_large_batch_is_fast():
     # writers copy it and the fourth finds it unshared and writes in place
     assert len(copies) == 3 * partial
     assert dt < 0.05
+
+
+@pytest.mark.parametrize("bs", [1, 16])
+def test_defrag_of_a_fragmented_pool_matches_the_model(bs):
+    """Twelve sequences (some forked), every other one dropped: defrag to a
+    partial target, then fully; moves, tables and counts as the model says."""
+    rng = np.random.default_rng(bs)
+    n_seqs, max_blocks = 12, 200 // bs + 2
+    n_blocks = n_seqs * max_blocks
+    lp = pkv.BlockPool(n_blocks, n_seqs, max_blocks, bs)
+    mp = BlockPoolModel(n_blocks, n_seqs, max_blocks, bs)
+    for s in range(0, n_seqs, 3):
+        n = int(rng.integers(20, 200))
+        lp.prepare_writes([s], [0], [n])
+        mp.prepare_writes([(s, 0, n)])
+        for d in (s + 1, s + 2):
+            lp.fork(s, d, n // 2)
+            mp.fork(s, d, n // 2)
+            lp.prepare_writes([d], [n // 2], [30])
+            mp.prepare_writes([(d, n // 2, 30)])
+    for s in range(0, n_seqs, 2):
+        lp.remove(s, 0, 1 << 30)
+        mp.remove(s, 0, 1 << 30)
+    _same(lp, mp)
+    total = 0
+    for need in (mp.n_free() // 3, -1, -1):
+        want = mp.defrag(need)
+        got = lp.defrag(need)
+        assert [tuple(m) for m in got.tolist()] == want
+        _same(lp, mp)
+        mp.check()
+        total += len(want)
+    assert total > 0
+    live = n_blocks - mp.n_free()
+    assert np.all(mp.ref[live:] == 0) and np.all(mp.ref[:live] > 0)
