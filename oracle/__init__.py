@@ -25,6 +25,8 @@ written from the source pages directly:
   model", and "KV Cache Design", sections 1-2: the copy-on-write block pool
   (forks share blocks by reference count; a write into a shared block
   copies it first, so readers of the shared prefix see no change).
+* "Tiered KV cache — architecture", section "The three-tier model": the
+  int4 cold-block codec (one f32 scale per block, packed nibbles).
 
 Arithmetic is float64 numpy; byte work is exact.  Readings of points the
 pages leave open are stated in the docstrings where they are used.
@@ -47,3 +49,4 @@ from .attention import (  # noqa: F401
 from .moves import order_moves, copy_cells, copy_cells_rowwise, provenance  # noqa: F401
 from .store import quantize_q8_0, encode_rows, destination_rows, store_rows  # noqa: F401
 from .cow import BlockPoolModel, copy_blocks  # noqa: F401
+from .int4 import blob_bytes, encode_block, decode_block, encode_blocks, cosine  # noqa: F401
