@@ -18,7 +18,7 @@ resident in HBM.  Prints one JSON line:
   workload on this host.
 
 Other workloads (for the record; the default is the headline): decode1,
-decode2, decode5, prefill4, copy5b, store4, cow3, defrag3; and calib, a plain device copy of known
+decode2, decode5, prefill4, copy5b, store4, cow3, defrag3, int4; and calib, a plain device copy of known
 size used to scale the HBM byte counters.
 
 Counter summary (turns two rocprofv3 --pmc runs, FETCH_SIZE then WRITE_SIZE,
@@ -682,13 +682,72 @@ def run_defrag(args):
     }
 
 
+def run_int4(args):
+    """int4 cold-block codec on the 7B-class block shape (8 kv heads x 16
+    slots x hd 128, f16: 32 KiB per block): encode 16,384 random blocks of a
+    2^15-block pool into blobs (f32 scale + 8 KiB of nibbles), then decode
+    them into 16,384 other blocks.  Each launch timed with HIP events after
+    a cache eviction."""
+    import torch
+
+    import paged_kv_cache_table_amd as pkv
+
+    rng = np.random.default_rng(6)
+    nb, n = 1 << 15, 16384
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    pool = torch.randn((nb, 8, 16, 128), generator=g, device="cuda").half()
+    perm = rng.permutation(nb)
+    src = torch.from_numpy(perm[:n].astype(np.int32)).cuda()
+    dst = torch.from_numpy(perm[n : 2 * n].astype(np.int32)).cuda()
+    elems = 8 * 16 * 128
+    blob = pkv.int4_blob_bytes(elems)
+    blobs = torch.zeros((n, (blob + 15) // 16 * 16), dtype=torch.uint8, device="cuda")
+    flush = ColdCache()
+    stream = torch.cuda.current_stream()
+    enc, dec = [], []
+    for it in range(args.warmup + args.steps):
+        flush()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        pkv.int4_encode(pool, src, blobs)
+        e[1].record(stream)
+        flush()
+        e[2].record(stream)
+        pkv.int4_decode(blobs, pool, dst)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            enc.append(e[0].elapsed_time(e[1]))
+            dec.append(e[2].elapsed_time(e[3]))
+    enc_ms, dec_ms = float(np.mean(enc)), float(np.mean(dec))
+    blk_bytes = elems * 2
+    bytes_each = n * (blk_bytes + blob)  # read a block, write a blob (encode) or the reverse (decode)
+    enc_gbs = bytes_each / (enc_ms * 1e-3) / 1e9
+    dec_gbs = bytes_each / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": "int4 cold-block codec: encode HBM GB/s (% HBM peak); decode alongside",
+        "value": round(enc_gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(enc_ms + dec_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 <-> int4", "data": "synthetic",
+        "config": {"workload": f"{n} random blocks of a 2^15-block pool, 8 kv heads x 16 slots x hd 128 f16 "
+                               f"(32 KiB) <-> {blob}-byte blobs; encode then decode into other blocks; "
+                               "cache evicted before each launch",
+                   "blocks": n, "bytes_per_launch": bytes_each},
+        "decode_GBps": round(dec_gbs, 1), "encode_ms": round(enc_ms, 5), "decode_ms": round(dec_ms, 5),
+        "roofline": {"bound": "hbm", "kernel": "int4_encode_kernel", "achieved": round(enc_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode3",
-                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "cow3", "defrag3", "calib"])
+                    choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "cow3", "defrag3", "int4", "calib"])
     ap.add_argument("--pmc-summary", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
     ap.add_argument("--split", type=int, default=0, help="decode split size in tokens (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -724,6 +783,8 @@ def main(argv=None):
         res = run_cow(args)
     elif args.workload == "defrag3":
         res = run_defrag(args)
+    elif args.workload == "int4":
+        res = run_int4(args)
     elif args.workload == "copy5b":
         res = run_copy(args)
     else:

@@ -377,6 +377,34 @@ pkv_status pkv_cow_apply(void* k_pool, void* v_pool, int32_t n_pool_blocks, int6
                          int64_t table_entries, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * int4 cold-block codec ("Tiered KV cache — architecture", section "The
+ * three-tier model": a cold block is one f32 scale followed by ceil(n / 2)
+ * bytes of packed int4 nibbles, one scale per block; about 0.99 cosine
+ * similarity against the original).  A block is one pool block of one pool
+ * taken flat in memory order: block_elems = n_kv_heads * block_size *
+ * head_dim values (a multiple of 8, at most 65536).  Quantizer, in binary32:
+ * scale = amax / 7; code = x / scale rounded to nearest, ties to even,
+ * clamped to [-7, 7]; amax = 0 gives scale 0 and zero codes.  Blob: the
+ * scale (little-endian f32), then byte j = code 2j (low nibble, two's
+ * complement) | code 2j+1 (high nibble).  Decoding writes scale * code,
+ * rounded to binary32 and then to the pool format (nearest-even).
+ *
+ * pool: device [n_pool_blocks][block_elems] of fmt (PKV_F16 or PKV_F32),
+ * 16-byte aligned.  blocks: device int32 [n] pool block ids.  blobs: device
+ * [n][blob_stride] bytes, 4-byte aligned, blob_stride >= blob bytes and a
+ * multiple of 4; bytes past a blob's end are not touched.  Encode of a
+ * block id outside the pool writes an all-zero blob; decode into one writes
+ * nothing.  Destination block ids of one decode call are distinct.
+ * ------------------------------------------------------------------------- */
+int64_t pkv_int4_blob_bytes(int64_t n_elts);
+pkv_status pkv_int4_encode(const void* pool, int32_t fmt, int32_t n_pool_blocks, int64_t block_elems,
+                           const int32_t* blocks, int32_t n, void* blobs, int64_t blob_stride,
+                           void* stream);
+pkv_status pkv_int4_decode(const void* blobs, int64_t blob_stride, int32_t n, void* pool, int32_t fmt,
+                           int32_t n_pool_blocks, int64_t block_elems, const int32_t* blocks,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * Debug export of the block-table/window resolver the attention kernels use.
  * rows_out: int32 [n_q_total][n_cand]: for query j and candidate index i of
  * its sequence's window enumeration (causal: positions 0..seq_len-1; span:

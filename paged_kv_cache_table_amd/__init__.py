@@ -56,6 +56,9 @@ EXPORTS = (
     "pkv_pool_defrag",
     "pkv_pool_export",
     "pkv_cow_apply",
+    "pkv_int4_blob_bytes",
+    "pkv_int4_encode",
+    "pkv_int4_decode",
     "pkv_resolve_rows",
     "pkv_last_error",
     "pkv_version",
@@ -125,6 +128,9 @@ def lib() -> ctypes.CDLL:
         "pkv_pool_defrag": (I32, [P, I32, P, I32, P]),
         "pkv_pool_export": (I32, [P, P, P]),
         "pkv_cow_apply": (I32, [P, P, I32, I64, I64, P, I32, P, I64, P]),
+        "pkv_int4_blob_bytes": (I64, [I64]),
+        "pkv_int4_encode": (I32, [P, I32, I32, I64, P, I32, P, I64, P]),
+        "pkv_int4_decode": (I32, [P, I64, I32, P, I32, I32, I64, P, P]),
         "pkv_resolve_rows": (I32, [SH, I32, P, P, P, P, I32, I32, P, I32, P, P]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_version": (ctypes.c_char_p, []),
@@ -541,3 +547,46 @@ def cow_apply(k_pool, v_pool, ops, table=None):
     _check(lib().pkv_cow_apply(_ptr(k_pool), _ptr(v_pool), nb, kb, vb, _ptr(ops), ops.shape[0], _ptr(table),
                                table.numel() if table is not None else 0, _stream(k_pool)))
     return k_pool, v_pool
+
+
+# ---------------------------------------------------------------------------
+# int4 cold-block codec
+
+
+def int4_blob_bytes(n_elts: int) -> int:
+    return int(lib().pkv_int4_blob_bytes(n_elts))
+
+
+def _int4_geometry(pool):
+    if pool.dtype not in (_torch().float16, _torch().float32) or not pool.is_contiguous():
+        raise TypeError("the int4 codec works on contiguous float16 or float32 pools")
+    return pool.shape[0], pool[0].numel(), _fmt_of(pool)
+
+
+def int4_encode(pool, blocks, blobs=None):
+    """Encode pool blocks (device int32 ids [n]) into blobs [n, stride]
+    (uint8, stride = blob bytes rounded up to 16; allocated if not given)."""
+    torch = _torch()
+    _i32(blocks, "blocks")
+    nb, elems, fmt = _int4_geometry(pool)
+    n = blocks.numel()
+    if blobs is None:
+        stride = (int4_blob_bytes(elems) + 15) // 16 * 16
+        blobs = torch.zeros((n, stride), dtype=torch.uint8, device=pool.device)
+    if blobs.dim() != 2 or blobs.shape[0] != n or not blobs.is_contiguous():
+        raise TypeError("blobs must be a contiguous [n, stride] uint8 tensor")
+    _check(lib().pkv_int4_encode(_ptr(pool), fmt, nb, elems, _ptr(blocks), n, _ptr(blobs), blobs.shape[1],
+                                 _stream(pool)))
+    return blobs
+
+
+def int4_decode(blobs, pool, blocks):
+    """Decode blobs [n, stride] into the listed pool blocks (device int32 [n])."""
+    _i32(blocks, "blocks")
+    nb, elems, fmt = _int4_geometry(pool)
+    n = blocks.numel()
+    if blobs.dim() != 2 or blobs.shape[0] != n or not blobs.is_contiguous():
+        raise TypeError("blobs must be a contiguous [n, stride] uint8 tensor")
+    _check(lib().pkv_int4_decode(_ptr(blobs), blobs.shape[1], n, _ptr(pool), fmt, nb, elems, _ptr(blocks),
+                                 _stream(pool)))
+    return pool

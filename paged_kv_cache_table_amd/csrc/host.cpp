@@ -716,4 +716,51 @@ pkv_status pkv_cow_apply(void* k_pool, void* v_pool, int32_t n_pool_blocks, int6
   return ok();
 }
 
+int64_t pkv_int4_blob_bytes(int64_t n_elts) { return n_elts < 0 ? 0 : 4 + (n_elts + 1) / 2; }
+
+namespace {
+pkv_status int4_call(bool encode, void* pool, int32_t fmt, int32_t n_pool_blocks, int64_t block_elems,
+                     const int32_t* blocks, int32_t n, void* blobs, int64_t blob_stride, void* stream) {
+  if (n < 0) return fail(PKV_E_ARG, "negative block count %d", n);
+  if (fmt != PKV_F16 && fmt != PKV_F32)
+    return fail(PKV_E_UNSUPPORTED, "the int4 codec reads and writes f16 or f32 pools, not %s", fmt_name(fmt));
+  if (n_pool_blocks <= 0) return fail(PKV_E_ARG, "n_pool_blocks %d must be positive", n_pool_blocks);
+  if (block_elems <= 0 || block_elems % 8 || block_elems > 65536)
+    return fail(PKV_E_UNSUPPORTED, "block_elems %lld must be a positive multiple of 8 up to 65536",
+                (long long)block_elems);
+  if (blob_stride < pkv_int4_blob_bytes(block_elems) || blob_stride % 4)
+    return fail(PKV_E_ARG, "blob_stride %lld must be a multiple of 4 of at least %lld bytes",
+                (long long)blob_stride, (long long)pkv_int4_blob_bytes(block_elems));
+  if (n == 0) return ok();
+  if (!pool || !blocks || !blobs) return fail(PKV_E_ARG, "pool, blocks and blobs must be non-NULL");
+  if (((uintptr_t)pool) % 16 || ((uintptr_t)blobs) % 4)
+    return fail(PKV_E_ARG, "the pool must be 16-byte and the blobs 4-byte aligned");
+  pkv::Int4Args a{};
+  a.pool = (unsigned char*)pool;
+  a.blobs = (unsigned char*)blobs;
+  a.blocks = blocks;
+  a.blob_stride = blob_stride;
+  a.block_elems = block_elems;
+  a.n = n;
+  a.n_pool_blocks = n_pool_blocks;
+  hipError_t e = pkv::launch_int4(encode, a, fmt, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, encode ? "int4 encode launch" : "int4 decode launch");
+  return ok();
+}
+}  // namespace
+
+pkv_status pkv_int4_encode(const void* pool, int32_t fmt, int32_t n_pool_blocks, int64_t block_elems,
+                           const int32_t* blocks, int32_t n, void* blobs, int64_t blob_stride,
+                           void* stream) {
+  return int4_call(true, (void*)pool, fmt, n_pool_blocks, block_elems, blocks, n, blobs, blob_stride,
+                   stream);
+}
+
+pkv_status pkv_int4_decode(const void* blobs, int64_t blob_stride, int32_t n, void* pool, int32_t fmt,
+                           int32_t n_pool_blocks, int64_t block_elems, const int32_t* blocks,
+                           void* stream) {
+  return int4_call(false, pool, fmt, n_pool_blocks, block_elems, blocks, n, (void*)blobs, blob_stride,
+                   stream);
+}
+
 }  // extern "C"

@@ -214,6 +214,17 @@ hipError_t launch_copy_runs(const PoolGeom& pool, const int32_t* moves, const in
                             int32_t n_moves, int32_t total_rows, hipStream_t st);
 hipError_t launch_zero_words(int32_t* p, int n, hipStream_t st);
 
+// int4 cold-block codec: n listed blocks of the pool <-> n blobs.
+struct Int4Args {
+  unsigned char* pool;   // [n_pool_blocks][block_elems] of f16 or f32 (read by encode)
+  unsigned char* blobs;  // [n][blob_stride]: f32 scale, then block_elems / 2 bytes
+  const int32_t* blocks; // [n] pool block ids
+  int64_t blob_stride, block_elems;
+  int32_t n, n_pool_blocks;
+};
+// Grid n x 512 threads.  block_elems % 8 == 0 and <= 65536.
+hipError_t launch_int4(bool encode, const Int4Args& a, int fmt, hipStream_t st);
+
 // Store of new K/V rows through the block table (pool[1] may be null).
 struct StoreArgs {
   const unsigned char* src[2];  // [n_tok][n_kv_heads][head_dim] of the source type
