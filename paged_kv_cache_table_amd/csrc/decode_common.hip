@@ -20,7 +20,7 @@ hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int
 }
 
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st) {
-  const dim3 grid(hd / 64, a.n_q_heads, a.n_seqs);
+  const dim3 grid((unsigned)((a.n_q_heads * hd + 255) / 256), a.n_seqs);
   switch (hd) {
     case 64: hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, st, a); break;
     case 128: hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, st, a); break;

@@ -433,67 +433,59 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split slots of one (sequence, q head) by log-sum-exp:
+// Merge the split slots of each (sequence, q head) by log-sum-exp:
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, lse = (M + log2 L) ln 2.
-// One workgroup per (64-wide slice of head_dim, q head, sequence); its four
-// waves take every fourth slot (lane = dimension), so four slot rows are in
-// flight per step, and combine through LDS in a fixed order.
+// One workgroup per (256 consecutive (q head, dim) outputs, sequence): each
+// thread owns one output and merges the slots in slot order with a running
+// max (rescaling when it grows), so a single pass suffices; the partial
+// loads of eight slots are issued before their arithmetic.  The merge order
+// is fixed, so results are deterministic.
 template <int HD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
-  const int dc = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  constexpr int kUnroll = 8;
+  const int s = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // q head * HD + dim
+  if (idx >= a.n_q_heads * HD) return;
+  const int h = idx / HD, d = idx - h * HD;
   const int nslot = a.n_runs * a.nspl;
   const int32_t lim = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
   const int64_t row0 = (int64_t)s * nslot * a.n_q_heads + h;  // slot stride n_q_heads
-  __shared__ float red[256];
-  __shared__ float red2[256];
-
-  float M = -INFINITY;
-  for (int slot = t; slot < nslot; slot += 256) {
-    int32_t lo, hi;
-    split_range(a, s, slot, lim, lo, hi);
-    if (lo < hi) M = fmaxf(M, a.part_ml[(row0 + (int64_t)slot * a.n_q_heads) * 2]);
-  }
-  red[t] = M;
-  __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (t < k) red[t] = fmaxf(red[t], red[t + k]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
-
-  const int d = dc * 64 + lane;
-  float acc = 0.f, lsum = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int slot = w; slot < nslot; slot += 4) {
-      int32_t lo, hi;
-      split_range(a, s, slot, lim, lo, hi);
-      if (lo >= hi) continue;
-      const int64_t r = row0 + (int64_t)slot * a.n_q_heads;
-      const float2 ml = *(const float2*)(a.part_ml + r * 2);
-      if (ml.x == -INFINITY) continue;
-      const float wgt = fast_exp2(ml.x - M);
-      acc = fmaf(wgt, a.part_o[r * HD + d], acc);
-      lsum = fmaf(wgt, ml.y, lsum);
+  float m = -INFINITY, l = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < nslot; s0 += kUnroll) {
+    float2 ml[kUnroll];
+    float o[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int slot = s0 + u;
+      ml[u] = make_float2(-INFINITY, 0.f);
+      o[u] = 0.f;
+      if (slot < nslot) {
+        int32_t lo, hi;
+        split_range(a, s, slot, lim, lo, hi);
+        if (lo < hi) {
+          const int64_t r = row0 + (int64_t)slot * a.n_q_heads;
+          ml[u] = *(const float2*)(a.part_ml + r * 2);
+          o[u] = a.part_o[r * HD + d];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (ml[u].x == -INFINITY) continue;  // a slot that saw nothing carries no weight
+      const float mn = fmaxf(m, ml[u].x);
+      const float ca = fast_exp2(m - mn), cb = fast_exp2(ml[u].x - mn);  // m = -inf -> ca = 0
+      acc = acc * ca + cb * o[u];
+      l = l * ca + cb * ml[u].y;
+      m = mn;
     }
   }
-  red[t] = acc;
-  red2[t] = lsum;
-  __syncthreads();
-  if (w == 0) {
-    const float sa = (red[lane] + red[64 + lane]) + (red[128 + lane] + red[192 + lane]);
-    const float sl = (red2[lane] + red2[64 + lane]) + (red2[128 + lane] + red2[192 + lane]);
-    const int64_t o = ((int64_t)s * a.n_q_heads + h) * HD + d;
-    if (M == -INFINITY) {
-      a.out[o] = 0.f;
-      if (a.lse && dc == 0 && lane == 0) a.lse[(int64_t)s * a.n_q_heads + h] = -INFINITY;
-    } else {
-      a.out[o] = sa / sl;
-      if (a.lse && dc == 0 && lane == 0)
-        a.lse[(int64_t)s * a.n_q_heads + h] = (M + __builtin_amdgcn_logf(sl)) * kLn2;
-    }
+  const int64_t oi = ((int64_t)s * a.n_q_heads + h) * HD + d;
+  if (m == -INFINITY) {
+    a.out[oi] = 0.f;
+    if (a.lse && d == 0) a.lse[(int64_t)s * a.n_q_heads + h] = -INFINITY;
+  } else {
+    a.out[oi] = acc / l;
+    if (a.lse && d == 0) a.lse[(int64_t)s * a.n_q_heads + h] = (m + __builtin_amdgcn_logf(l)) * kLn2;
   }
 }
 

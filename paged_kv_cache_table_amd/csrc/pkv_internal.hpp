@@ -189,7 +189,7 @@ __device__ __forceinline__ float h2f_hi(uint32_t w) {
 // Decode split pass: grid (n_kv_heads, n_runs * nspl, n_seqs), 64 threads.
 hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int g, hipStream_t st,
                                bool* found);
-// Decode merge pass: grid (head_dim / 64, n_q_heads, n_seqs), 256 threads.
+// Decode merge pass: grid (ceil(n_q_heads * head_dim / 256), n_seqs), 256 threads.
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
 // Prefill: workspace bytes a call needs (a multiple of 256, the last 256
 // bytes hold the checked-mode error word; 0 if none) and whether a kernel
