@@ -465,28 +465,29 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
           // the even lane of each lane pair: take it from there
           const uint32_t sw = ok ? (sh ? (qw[0] >> 16) : (qw[0] & 0xFFFFu)) : 0u;
           const uint32_t sw0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sw, 0xA0, 0xF, 0xF, false);
-          const float sc8 = (float)__builtin_bit_cast(_Float16, (unsigned short)sw0);
-          // x = scale * code exactly: with u = code + 128 (sign bit flipped),
-          // x = u * scale - 128 * scale, both products exact, one rounding
-          // of an exactly representable sum
-          const float nb = -128.f * sc8;
+          const _Float16 s16 = __builtin_bit_cast(_Float16, (unsigned short)sw0);
+          const half2_t s2 = {s16, s16};
+          // x = scale * code exactly as hi + lo, two values per instruction:
+          // hi = RN16(code * scale) (packed multiply); code * scale has at
+          // most 18 significant bits, all multiples of the scale's ulp
+          // (>= 2^-24), so lo = code * scale - hi fits an f16 and the packed
+          // fused multiply-add computes it exactly
           half8_t hi8[2], lo8[2];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const uint32_t y = cw[i] ^ 0x80808080u;
-            const float x0 = fmaf((float)(y & 0xFFu), sc8, nb);
-            const float x1 = fmaf((float)((y >> 8) & 0xFFu), sc8, nb);
-            const float x2 = fmaf((float)((y >> 16) & 0xFFu), sc8, nb);
-            const float x3 = fmaf((float)(y >> 24), sc8, nb);
-            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
-            hi8[i >> 1][4 * (i & 1) + 0] = h0;
-            hi8[i >> 1][4 * (i & 1) + 1] = h1;
-            hi8[i >> 1][4 * (i & 1) + 2] = h2;
-            hi8[i >> 1][4 * (i & 1) + 3] = h3;
-            lo8[i >> 1][4 * (i & 1) + 0] = (_Float16)(x0 - (float)h0);
-            lo8[i >> 1][4 * (i & 1) + 1] = (_Float16)(x1 - (float)h1);
-            lo8[i >> 1][4 * (i & 1) + 2] = (_Float16)(x2 - (float)h2);
-            lo8[i >> 1][4 * (i & 1) + 3] = (_Float16)(x3 - (float)h3);
+            half2_t c01, c23;
+            codes_to_f16(cw[i], c01, c23);
+            const half2_t h01 = c01 * s2, h23 = c23 * s2;
+            const half2_t l01 = __builtin_elementwise_fma(c01, s2, -h01);
+            const half2_t l23 = __builtin_elementwise_fma(c23, s2, -h23);
+            hi8[i >> 1][4 * (i & 1) + 0] = h01[0];
+            hi8[i >> 1][4 * (i & 1) + 1] = h01[1];
+            hi8[i >> 1][4 * (i & 1) + 2] = h23[0];
+            hi8[i >> 1][4 * (i & 1) + 3] = h23[1];
+            lo8[i >> 1][4 * (i & 1) + 0] = l01[0];
+            lo8[i >> 1][4 * (i & 1) + 1] = l01[1];
+            lo8[i >> 1][4 * (i & 1) + 2] = l23[0];
+            lo8[i >> 1][4 * (i & 1) + 3] = l23[1];
           }
 #pragma unroll
           for (int e2 = 0; e2 < 2; ++e2) {
