@@ -81,17 +81,38 @@ def test_decode_split_sizes(split):
     compare(out, lse, ro, rl, tol_of(w), f"split {split}")
 
 
-def test_partials_then_merge_equals_fused():
+@pytest.mark.parametrize("case", ["w3", "kv_map_holes", "degenerate"])
+def test_one_call_equals_partials_then_merge(case):
+    """One call equals the two-call route (partials, then merge) bit for bit,
+    also on a dirty workspace, on repeat calls and on sequences with no
+    visible position (out 0, lse -inf)."""
     import torch
 
-    w = wgen.make(3, small=True)
+    if case == "w3":
+        w = wgen.make(3, small=True)
+    else:
+        w = wgen.make_custom(seed=91, n_seqs=9, n_q_heads=16, n_kv_heads=4, head_dim=128, block_size=16,
+                             ctx=(0, 700), mode="kv_map", n_runs=5, hole_frac=0.2)
+        if case == "degenerate":
+            w.kv_map[0] = 0                 # no runs: empty window
+            w.block_table[1, :] = -1        # all holes
+            w.seq_lens[2] = 0               # empty sequence
     d = Dev(w)
-    out1, lse1 = d.decode()
-    ws = torch.empty(pkv.decode_workspace_bytes(pkv.make_shape(d.q, d.k, d.v, d.table, w.n_seqs, w.scale)),
+    ws = torch.empty(pkv.decode_workspace_bytes(pkv.make_shape(d.q, d.k, d.v, d.table, w.n_seqs, w.scale),
+                                                w.mode, 1 if w.mode != "kv_map" else w.kv_map.shape[1]),
                      dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)  # nothing may depend on the workspace's previous contents
+    out1, lse1 = d.decode(workspace=ws)
+    out1b, lse1b = d.decode(workspace=ws)
     d.decode(part="partials", workspace=ws)
     out2, lse2 = d.decode(part="merge", workspace=ws)
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    assert torch.equal(out1, out1b) and torch.equal(lse1, lse1b)
+    if case == "degenerate":
+        assert torch.all(out1[:3] == 0) and torch.all(torch.isneginf(lse1[:3]))
+    if case != "w3":
+        ro, rl = d.oracle()
+        compare(out1.cpu().numpy(), lse1.cpu().numpy(), ro, rl, tol_of(w), case)
 
 
 def test_determinism_and_block_permutation_invariance():
