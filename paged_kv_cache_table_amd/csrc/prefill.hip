@@ -531,8 +531,9 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
 
   // One tile, in 32-position halves: the online softmax is exact in any
   // order, so each half updates the running max/sum and the output in turn.
-  // The scores of the next half are issued (matrix cores) before the
-  // softmax of the current half (vector ALU), so the two overlap.
+  // The scores of the next half (matrix cores) are issued after the running
+  // max of the current half and interleaved with its exponentials (vector
+  // ALU), so the two overlap.
   auto compute = [&](int sl, int kb, const TileD& d) {
     const unsigned char* kt = KQ8 ? sm.k[kb][0] : sm.k[sl][0];
     const unsigned char* vt = sm.v[sl];
@@ -546,7 +547,6 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) sc[rt][jj] = sn[rt][jj];
-      if (kh + 1 < NKH) scores(kt, kh + 1, sn);
       const uint32_t vmh = (uint32_t)(d.vm >> (32 * kh));
       const int32_t t0h = d.t0 + 32 * kh;
       const bool full = vmh == 0xffffffffu && t0h + 32 <= lim_min_w;
@@ -582,9 +582,14 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
           for (int dt = 0; dt <= DT; ++dt) o[rt][dt] *= alpha;
           m[rt] = mn;
         }
+      }
+      // the next half's scores (matrix cores) next to this half's
+      // exponentials (vector ALU): one basic block, so they interleave
+      if (kh + 1 < NKH) scores(kt, kh + 1, sn);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) pf[rt][jj] = (_Float16)fast_exp2(fmaf(sc[rt][jj], mul, -m[rt]));
-      }
 
       // ---- O^T += V^T P^T: two transposing reads give lane (g, n16) column
       // dt*16 + n16 of V at positions 16 h + 4 g + e of the half (operand
@@ -611,6 +616,30 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       // row sums of the rounded probabilities (every element of o[rt][DT])
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) o[rt][DT] = mfma16x16x32(ones, pf[rt], o[rt][DT]);
+      // Issue order of this block (a scheduling hint; no effect on values):
+      // the K fragment reads run four ahead of the matrix instructions that
+      // use them, three vector instructions (the exponentials) sit between
+      // each pair of score MFMAs, and the V reads of the PV step again run
+      // four ahead.  Masks: 0x100 LDS read, 0x008 MFMA, 0x002 vector ALU.
+      if (kh + 1 < NKH) {
+        constexpr int kSM = 2 * KS * RT * (KQ8 ? 2 : 1);  // score MFMAs of a half
+        constexpr int kSR = 2 * KS * (KQ8 ? 2 : 1);       // their K fragment reads
+        constexpr int kPM = (DT + 1) * RT;                // PV and row-sum MFMAs
+        constexpr int kPR = 2 * DT;                       // V reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < kSM / 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          if (i < kSR - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < kPM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < kPR - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
     }
   };
 
