@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -270,23 +271,46 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
 // order_moves: indices of the effective moves, upward moves (dst > src) by
 // descending src then descending dst, then downward moves by ascending src
 // then ascending dst; ties by input index.
+// Stable LSD radix sort of (key, index) pairs by key, 8 bits per pass;
+// passes whose digit is the same for every key are skipped.
+void radix_sort_pairs(std::vector<std::pair<uint64_t, int32_t>>* v) {
+  std::vector<std::pair<uint64_t, int32_t>> tmp(v->size());
+  uint64_t all_or = 0, all_and = ~0ull;
+  for (const auto& x : *v) {
+    all_or |= x.first;
+    all_and &= x.first;
+  }
+  for (int shift = 0; shift < 64; shift += 8) {
+    if ((((all_or ^ all_and) >> shift) & 0xFF) == 0) continue;  // constant digit
+    size_t count[257] = {0};
+    for (const auto& x : *v) ++count[((x.first >> shift) & 0xFF) + 1];
+    for (int b = 0; b < 256; ++b) count[b + 1] += count[b];
+    for (const auto& x : *v) tmp[count[(x.first >> shift) & 0xFF]++] = x;
+    v->swap(tmp);
+  }
+}
+
+// order_moves: moves with dst > src first, by src then dst descending; then
+// moves with dst < src, by src then dst ascending; ties keep input order.
+// Moves with len <= 0 or src == dst are dropped.  (Keys are built so that an
+// ascending stable sort gives that order: flipping the sign bit maps int32
+// onto uint32 in order, and 2^32 - 1 - x reverses it.)
 std::vector<int32_t> order_moves_impl(const int32_t* mv, int32_t n) {
-  std::vector<int32_t> up, down;
+  std::vector<std::pair<uint64_t, int32_t>> up, down;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t s = mv[3 * i], d = mv[3 * i + 1], len = mv[3 * i + 2];
     if (len <= 0 || d == s) continue;
-    (d > s ? up : down).push_back(i);
+    const uint64_t us = (uint32_t)s ^ 0x80000000u, ud = (uint32_t)d ^ 0x80000000u;
+    if (d > s) up.push_back({((0xFFFFFFFFull - us) << 32) | (0xFFFFFFFFull - ud), i});
+    else down.push_back({(us << 32) | ud, i});
   }
-  std::stable_sort(up.begin(), up.end(), [&](int32_t a, int32_t b) {
-    if (mv[3 * a] != mv[3 * b]) return mv[3 * a] > mv[3 * b];
-    return mv[3 * a + 1] > mv[3 * b + 1];
-  });
-  std::stable_sort(down.begin(), down.end(), [&](int32_t a, int32_t b) {
-    if (mv[3 * a] != mv[3 * b]) return mv[3 * a] < mv[3 * b];
-    return mv[3 * a + 1] < mv[3 * b + 1];
-  });
-  up.insert(up.end(), down.begin(), down.end());
-  return up;
+  radix_sort_pairs(&up);
+  radix_sort_pairs(&down);
+  std::vector<int32_t> o;
+  o.reserve(up.size() + down.size());
+  for (const auto& x : up) o.push_back(x.second);
+  for (const auto& x : down) o.push_back(x.second);
+  return o;
 }
 
 // The effective moves (len > 0, src != dst) as (src, dst, len), and whether
@@ -295,25 +319,62 @@ std::vector<int32_t> order_moves_impl(const int32_t* mv, int32_t n) {
 // same bytes and all rows can be copied at once.
 bool disjoint_moves(const int32_t* mv, int32_t n, std::vector<int32_t>* eff) {
   eff->clear();
-  std::vector<std::pair<int64_t, int64_t>> src, dst;
   for (int32_t i = 0; i < n; ++i) {
     const int64_t s = mv[3 * i], d = mv[3 * i + 1], len = mv[3 * i + 2];
     if (len <= 0 || s == d) continue;
+    if (s < d + len && d < s + len) return false;  // a move overlapping itself (a slide)
     eff->insert(eff->end(), {(int32_t)s, (int32_t)d, (int32_t)len});
+  }
+  const size_t m = eff->size() / 3;
+  std::vector<std::pair<int64_t, int64_t>> src, dst;
+  src.reserve(m);
+  dst.reserve(m);
+  for (size_t i = 0; i < m; ++i) {
+    const int64_t s = (*eff)[3 * i], d = (*eff)[3 * i + 1], len = (*eff)[3 * i + 2];
     src.push_back({s, s + len});
     dst.push_back({d, d + len});
   }
-  std::sort(src.begin(), src.end());
   std::sort(dst.begin(), dst.end());
   for (size_t i = 1; i < dst.size(); ++i)
-    if (dst[i].first < dst[i - 1].second) return false;
-  size_t j = 0;  // sweep: sources ending after the current destination's start
-  for (const auto& d : dst) {
-    while (j < src.size() && src[j].second <= d.first) ++j;
-    for (size_t k = j; k < src.size() && src[k].first < d.second; ++k)
-      if (src[k].second > d.first) return false;
+    if (dst[i].first < dst[i - 1].second) return false;  // two destinations overlap
+  std::sort(src.begin(), src.end());
+  // destinations are disjoint and sorted; a source overlaps one iff the
+  // first destination ending after the source's start begins before its end
+  size_t j = 0;
+  for (const auto& sr : src) {
+    while (j < dst.size() && dst[j].second <= sr.first) ++j;
+    if (j < dst.size() && dst[j].first < sr.second) return false;
   }
   return true;
+}
+
+// Pinned host staging for plan uploads: grown to the largest plan so far and
+// kept until the process ends; one upload at a time.
+std::mutex g_stage_mu;
+void* g_stage = nullptr;
+size_t g_stage_bytes = 0;
+
+// Copies `bytes` from host memory to device memory `dst` through the pinned
+// stage and waits for the copy (and the work queued before it on `st`).
+hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return hipSuccess;
+  std::lock_guard<std::mutex> lock(g_stage_mu);
+  if (g_stage_bytes < bytes) {
+    if (g_stage) (void)hipHostFree(g_stage);
+    g_stage = nullptr;
+    g_stage_bytes = 0;
+    const size_t want = std::max(bytes, (size_t)1 << 20);
+    hipError_t e = hipHostMalloc(&g_stage, want, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      g_stage = nullptr;
+      return e;
+    }
+    g_stage_bytes = want;
+  }
+  std::memcpy(g_stage, src, bytes);
+  hipError_t e = hipMemcpyAsync(dst, g_stage, bytes, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e;
 }
 
 }  // namespace
@@ -512,8 +573,7 @@ pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, 
     if (!ws || ws_bytes < need)
       return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                   ws ? ws_bytes : (size_t)0, need);
-    hipError_t e = hipMemcpyAsync(ws, up.data(), up.size() * sizeof(int32_t), hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    hipError_t e = upload(ws, up.data(), up.size() * sizeof(int32_t), st);
     if (e != hipSuccess) return device_fail(e, "uploading the moves");
     const int32_t* d_moves = (const int32_t*)ws;
     const int32_t* d_cum = d_moves + eff.size();
@@ -572,9 +632,7 @@ pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, 
   idx.insert(idx.end(), scatter.begin(), scatter.end());
   int32_t* d_idx = (int32_t*)ws;
   unsigned char* stage = (unsigned char*)ws + idx_bytes;
-  hipError_t e = hipMemcpyAsync(d_idx, idx.data(), idx.size() * sizeof(int32_t),
-                                hipMemcpyHostToDevice, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  hipError_t e = upload(d_idx, idx.data(), idx.size() * sizeof(int32_t), st);
   if (e != hipSuccess) return device_fail(e, "uploading the move plan");
   const int32_t n_gather = (int32_t)(gather.size() / 2), n_scatter = (int32_t)(scatter.size() / 2);
   const int32_t* d_gather = d_idx;

@@ -64,6 +64,10 @@ def test_order_moves_golden_and_random():
         assert pkv.order_moves(mv) == oracle.order_moves(mv)
     ms = wgen.make_moves(seed=55, n_moves=10000)
     assert pkv.order_moves(ms.moves) == oracle.order_moves(ms.moves)
+    for _ in range(200):  # negative rows (order_moves takes any int32) and runs of equal keys
+        n = int(rng.integers(1, 50))
+        mv = np.stack([rng.integers(-4, 4, n), rng.integers(-4, 4, n), rng.integers(-1, 3, n)], 1)
+        assert pkv.order_moves(mv) == oracle.order_moves(mv)
 
 
 def _shape(**kw):
@@ -178,3 +182,37 @@ def test_copy_cells_workspace_for_disjoint_moves_is_small():
     overlapping = np.array([[0, 5, 10], [200, 20, 30]], dtype=np.int32)  # 0..9 -> 5..14 overlaps itself
     big = pkv.lib().pkv_copy_cells_workspace_bytes(overlapping.ctypes.data, 2, 4096, 4096)
     assert big >= 40 * 4096
+
+
+def _disjoint_brute(mv):
+    """No destination row is written twice and no destination row is read."""
+    dst, src = [], []
+    for a, b, n in mv.tolist():
+        if n <= 0 or a == b:
+            continue
+        dst += range(b, b + n)
+        src += range(a, a + n)
+    return len(dst) == len(set(dst)) and not (set(dst) & set(src))
+
+
+def test_copy_cells_disjoint_check():
+    """The workspace is the small one exactly when the moves are disjoint,
+    for dense and sparse move sets (some disjoint by construction), checked
+    against a row-by-row brute force."""
+    rng = np.random.default_rng(9)
+    seen = {True: 0, False: 0}
+    for t in range(400):
+        n = int(rng.integers(1, 12))
+        span = 200 if t % 2 else 1 << 22  # dense, then sparse over a wide row range
+        mv = np.stack([rng.integers(0, span, n), rng.integers(0, span, n), rng.integers(-1, 9, n)], 1)
+        if t % 4 == 1:  # disjoint by construction: destinations above every source
+            mv[:, 1] = span + 16 * np.arange(n)
+            mv[:, 2] = np.clip(mv[:, 2], 0, 16)
+        mv = mv.astype(np.int32)
+        m = int(np.sum((mv[:, 2] > 0) & (mv[:, 0] != mv[:, 1])))
+        small_bound = (3 * m + m + 1) * 4 // 256 * 256 + 512
+        ws = pkv.lib().pkv_copy_cells_workspace_bytes(mv.ctypes.data, n, 4096, 4096)
+        want = _disjoint_brute(mv)
+        assert (ws <= small_bound) == want or m == 0, (t, mv.tolist(), ws)
+        seen[want] += 1
+    assert seen[True] > 50 and seen[False] > 50
