@@ -48,11 +48,11 @@ CALIB_BYTES = 4 << 30  # bytes read and bytes written by one calibration copy
 _CSRC = "paged_kv_cache_table_amd/csrc/"
 TRAFFIC = {
     "decode3": ("profiles/decode_split_7b_class.traffic.json",
-                ("include/pkv.h", _CSRC + "pkv_internal.hpp", _CSRC + "decode_impl.hpp", _CSRC + "decode_f16.hip")),
+                (_CSRC + "pkv_internal.hpp", _CSRC + "decode_impl.hpp", _CSRC + "decode_f16.hip")),
     "store4": ("profiles/store_w4.traffic.json",
-               ("include/pkv.h", _CSRC + "pkv_internal.hpp", _CSRC + "store.hip")),
+               (_CSRC + "pkv_internal.hpp", _CSRC + "store.hip")),
     "prefill4": ("profiles/prefill_window_w4.traffic.json",
-                 ("include/pkv.h", _CSRC + "pkv_internal.hpp", _CSRC + "prefill.hip")),
+                 (_CSRC + "pkv_internal.hpp", _CSRC + "prefill.hip")),
 }
 MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + queries/s"

@@ -219,9 +219,13 @@ size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t r
  * multiple of 4); a row is one slot of every kv head, so a move carries all
  * kv heads of its tokens.  The host plans the moves (order_moves, then the
  * final source of every changed row), uploads the plan into the workspace
- * and waits for that upload, so `moves` may be freed on return; the copies
- * run asynchronously on `stream`.  Every move must lie inside
- * [0, n_pool_blocks * block_size) or the call is refused untouched. */
+ * and waits for that upload (and so for the work queued before it on
+ * `stream`), so `moves` may be freed on return; the copies run
+ * asynchronously on `stream`.  The upload goes through a pinned host buffer
+ * that the library allocates on first use, grows to the largest plan seen
+ * and keeps until the process ends; concurrent calls take turns on it.
+ * Every move must lie inside [0, n_pool_blocks * block_size) or the call is
+ * refused untouched. */
 pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, int32_t block_size,
                              int32_t n_kv_heads, int64_t seg_bytes_k, int64_t seg_bytes_v,
                              const int32_t* moves, int32_t n, void* workspace,
