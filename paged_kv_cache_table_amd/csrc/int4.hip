@@ -108,16 +108,37 @@ __global__ __launch_bounds__(kI4Threads) void int4_encode_kernel(Int4Args a) {
   for (int w = 1; w < kI4Waves; ++w) amax = fmaxf(amax, wmax[w]);
   const float scale = amax / 7.0f;
   if (t == 0) *(float*)blob = ok ? scale : 0.f;
+  // code = rint(x / scale) with the binary32 division.  Fast form: with
+  // r = RN(1 / scale) and |x / scale| <= 7, t = RN(x * r) is within 2^-20 of
+  // x / scale, so rint(t) is the code unless t lies within 2^-18 of a
+  // half-integer (then RN(x / scale) could sit on the other side of it, or
+  // on it); those elements, and blocks whose scale is extreme, take the
+  // division.  |t - rint(t)| and its distance to 1/2 are exact in binary32.
+  const bool fast = scale >= 0x1p-100f && scale <= 0x1p+100f;
+  const float r = 1.0f / scale;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int64_t gi = (int64_t)c * kI4Threads + t;
     if (gi >= groups) continue;
     uint32_t word = 0;
     if (ok && scale > 0.f) {
+      float q[8];
+      bool slow = !fast;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int q = (int)fminf(fmaxf(rintf(g[c].at(i) / scale), -7.f), 7.f);
-        word |= (uint32_t)(q & 0xF) << (4 * i);
+        const float x = g[c].at(i);
+        const float tq = x * r;
+        q[i] = rintf(tq);
+        slow |= fabsf(fabsf(tq - q[i]) - 0.5f) <= 0x1p-18f;
+      }
+      if (slow) {  // rare: redo the group with the division
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = rintf(g[c].at(i) / scale);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int code = (int)fminf(fmaxf(q[i], -7.f), 7.f);
+        word |= (uint32_t)(code & 0xF) << (4 * i);
       }
     }
     *(uint32_t*)(blob + 4 + gi * 4) = word;
