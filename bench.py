@@ -254,18 +254,35 @@ def run_decode(cfg, args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    b_log, b_uniq_kv, vis = decode_bytes(w)
+    # A batch whose K/V fit in the 256 MB Infinity Cache would be timed from
+    # the cache: evict before every timed step and time each step with events
+    # (the eviction itself stays outside); the warm figure is kept, labelled.
+    cold = b_uniq_kv < (1 << 30)
+    flush = ColdCache() if cold else None
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    log(f"[bench] timing {args.steps} steps" + (" (caches evicted before each)" if cold else ""))
+    warm_ms = None
+    if cold:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        for i in range(args.steps):
+            flush()
+            step(evs[i])
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     split_ms = [e[0].elapsed_time(e[1]) for e in evs]
     merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    ms = wall * 1e3 / args.steps
-    b_log, b_uniq_kv, vis = decode_bytes(w)
+    ms = float(np.mean(step_ms)) if cold else wall * 1e3 / args.steps
     # algorithmic bytes of one split launch: unique K/V rows + q + table
     # entries read + seq_lens + partials written
     q_bytes = q.numel() * q.element_size()
@@ -300,6 +317,8 @@ def run_decode(cfg, args):
             "B_uniq_kv_bytes": int(b_uniq_kv),
             "split_tokens": int(split),
         },
+        "timing": ("HIP events per step, caches evicted before each step" if cold
+                   else "wall clock over back-to-back steps"),
         "queries_per_s": round(w.n_seqs / (ms * 1e-3), 1),
         "hbm_frac_uniq_step": round(b_uniq_kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "event_ms": {"step_median": round(float(np.median(step_ms)), 5),
@@ -316,6 +335,9 @@ def run_decode(cfg, args):
             "algorithmic_bytes": int(alg),
         },
     }
+    if warm_ms is not None:
+        res["warm_unflushed"] = {"ms_per_step": round(warm_ms, 5),
+                                 "GBps_B_log": round(b_log / (warm_ms * 1e-3) / 1e9, 2)}
     return res, w, {"q": q, "k": k, "v": v}
 
 
