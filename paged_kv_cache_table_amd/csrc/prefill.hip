@@ -572,10 +572,12 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
         float mx = sc[rt][0];
 #pragma unroll
         for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[rt][jj]);
-        mx = max_over_groups(mx);
-        const float mc = mx * mul;
-        const bool grow = mc > m[rt] + kLazyMax;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
+        // A row grows iff one of its lanes holds a score above the threshold
+        // (scaling by mul > 0 keeps the order), so the row max across the
+        // lane groups is only formed when some row of the wave grows.
+        if (__builtin_amdgcn_ballot_w64(mx * mul > m[rt] + kLazyMax)) {
+          const float mc = max_over_groups(mx) * mul;
+          const bool grow = mc > m[rt] + kLazyMax;
           const float mn = grow ? mc : m[rt];
           const float alpha = fast_exp2(m[rt] - mn);
 #pragma unroll
