@@ -167,7 +167,27 @@ def _torch():
 
 
 def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor argument (kernels dereference it)."""
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise TypeError(f"expected a GPU tensor, got one on {t.device}")
+    return t.data_ptr()
+
+
+def _on_one_gpu(*tensors):
+    """Every given tensor lives on the same GPU (None entries are skipped):
+    a host pointer or another GPU's memory handed to a kernel would fault."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise TypeError(f"expected GPU tensors, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise TypeError(f"tensors on {dev} and {t.device}: all must be on one GPU")
 
 
 def _stream(t) -> int:
@@ -255,6 +275,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, mo
     [S, n_runs, 2] (kv_map).  Returns (out float32 [S, Hq, hd], lse float32 [S, Hq]).
     part = "partials" / "merge" runs one of the two passes (same workspace)."""
     torch = _torch()
+    _on_one_gpu(q, k_pool, v_pool, block_table, seq_lens, window, out, lse, workspace)
     S = q.shape[0]
     shape = make_shape(q, k_pool, v_pool, block_table, S, scale, flags, split_tokens)
     _i32(seq_lens, "seq_lens")
@@ -298,6 +319,7 @@ def paged_attn_prefill_window(q, cu_q, q_pos, k_pool, v_pool, block_table, seq_l
     """Windowed prefill: queries of sequence s are rows cu_q[s]..cu_q[s+1]-1 of q
     [Nq, Hq, hd] at positions q_pos [Nq].  Returns (out [Nq, Hq, hd], lse [Nq, Hq])."""
     torch = _torch()
+    _on_one_gpu(q, cu_q, q_pos, k_pool, v_pool, block_table, seq_lens, window, out, lse, workspace)
     S = block_table.shape[0]
     Nq = q.shape[0]
     shape = make_shape(q, k_pool, v_pool, block_table, S, scale, flags)
@@ -322,6 +344,7 @@ def resolve_rows(block_table, seq_lens, block_size: int, n_kv_heads: int, head_d
                  k_fmt: int = F16, v_fmt: int = F16, q_fmt: int = F16):
     """Pool row read by every (query, window candidate), or -1 (debug export)."""
     torch = _torch()
+    _on_one_gpu(block_table, seq_lens, window, cu_q, q_pos)
     S = block_table.shape[0]
     shape = Shape(n_seqs=S, n_q_heads=n_q_heads or n_kv_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
                   block_size=block_size, n_pool_blocks=n_pool_blocks, max_blocks_per_seq=block_table.shape[1],
@@ -358,6 +381,7 @@ def kv_copy_cells(k_pool, v_pool, moves, workspace=None):
     import numpy as np
 
     torch = _torch()
+    _on_one_gpu(k_pool, v_pool, workspace)
     mv = np.ascontiguousarray(np.asarray(moves, dtype=np.int32).reshape(-1, 3))
     n = mv.shape[0]
     for t in (k_pool, v_pool):
@@ -390,6 +414,7 @@ def kv_store(k_new, v_new, positions, k_pool, v_pool, block_table, seq_ids=None,
     left out and counted into ``skipped`` (a device int32 tensor of one
     element, cleared by the caller) when it is given."""
     torch = _torch()
+    _on_one_gpu(k_new, v_new, positions, k_pool, v_pool, block_table, seq_ids, skipped)
     if k_new.dtype not in (torch.float32, torch.float16):
         raise TypeError("k_new must be float32 or float16")
     if (v_new is None) != (v_pool is None):
@@ -529,6 +554,7 @@ def cow_apply(k_pool, v_pool, ops, table=None):
     table is given (int32 [n_seqs, max_blocks]), patch its entries.  ops is
     a device int32 tensor [n, 3] or a host array (uploaded first)."""
     torch = _torch()
+    _on_one_gpu(k_pool, v_pool, table, ops if isinstance(ops, torch.Tensor) else None)
     if not isinstance(ops, torch.Tensor):
         import numpy as np
 
@@ -567,6 +593,7 @@ def int4_encode(pool, blocks, blobs=None):
     """Encode pool blocks (device int32 ids [n]) into blobs [n, stride]
     (uint8, stride = blob bytes rounded up to 16; allocated if not given)."""
     torch = _torch()
+    _on_one_gpu(pool, blocks, blobs)
     _i32(blocks, "blocks")
     nb, elems, fmt = _int4_geometry(pool)
     n = blocks.numel()
@@ -582,6 +609,7 @@ def int4_encode(pool, blocks, blobs=None):
 
 def int4_decode(blobs, pool, blocks):
     """Decode blobs [n, stride] into the listed pool blocks (device int32 [n])."""
+    _on_one_gpu(blobs, pool, blocks)
     _i32(blocks, "blocks")
     nb, elems, fmt = _int4_geometry(pool)
     n = blocks.numel()

@@ -216,3 +216,28 @@ def test_copy_cells_disjoint_check():
         assert (ws <= small_bound) == want or m == 0, (t, mv.tolist(), ws)
         seen[want] += 1
     assert seen[True] > 50 and seen[False] > 50
+
+
+def test_binding_refuses_host_tensors():
+    """Tensors that are not on a GPU are refused before anything reaches
+    the library (a kernel handed a host pointer would fault)."""
+    import torch
+
+    q = torch.zeros((2, 8, 128), dtype=torch.float16)
+    k = torch.zeros((4, 2, 16, 128), dtype=torch.float16)
+    table = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(TypeError, match="GPU"):
+        pkv.paged_attn_decode(q, k, k, table, lens, 0.1)
+    with pytest.raises(TypeError, match="GPU"):
+        pkv.kv_copy_cells(k, k, np.array([[0, 16, 4]], dtype=np.int32))
+    with pytest.raises(TypeError, match="GPU"):
+        pkv.kv_store(torch.zeros((1, 2, 128)), torch.zeros((1, 2, 128)), torch.zeros(1, dtype=torch.int32),
+                     k.float(), k.float(), table)
+    with pytest.raises(TypeError, match="GPU"):
+        pkv.int4_encode(k, torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(TypeError, match="GPU"):
+        pkv.cow_apply(k, k, np.zeros((1, 3), dtype=np.int32), table)
+    with pytest.raises(TypeError, match="GPU"):
+        pkv.paged_attn_prefill_window(q, torch.tensor([0, 1, 2], dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                                      k, k, table, lens, 0.1, 1, mode="causal")
