@@ -229,10 +229,30 @@ def make_shape(q, k_pool, v_pool, block_table, n_seqs: int, scale: float, flags:
     nb, hkv, bs, hd = v_pool.shape
     if tuple(k_pool.shape[:3]) != (nb, hkv, bs):
         raise TypeError("k_pool and v_pool disagree on (n_blocks, n_kv_heads, block_size)")
+    kw = row_bytes(_fmt_of(k_pool), 1, hd) // k_pool.element_size()
+    if k_pool.shape[3] != kw:
+        raise TypeError(f"k_pool rows are {k_pool.shape[3]} wide; head_dim {hd} in its format needs {kw}")
+    if q.dim() != 3 or q.shape[-1] != hd:
+        raise TypeError(f"q must be [n, n_q_heads, {hd}]")
+    if block_table.dim() != 2 or block_table.shape[0] < n_seqs:
+        raise TypeError(f"block_table must be [>= {n_seqs}, max_blocks]")
     return Shape(n_seqs=n_seqs, n_q_heads=q.shape[-2], n_kv_heads=hkv, head_dim=hd, block_size=bs,
                  n_pool_blocks=nb, max_blocks_per_seq=block_table.shape[1], q_fmt=_fmt_of(q),
                  k_fmt=_fmt_of(k_pool), v_fmt=_fmt_of(v_pool), scale=scale, flags=flags,
                  split_tokens=split_tokens)
+
+
+def _sized(t, name: str, numel: int, dtype=None):
+    """t (if given) is a contiguous tensor of at least `numel` elements of
+    `dtype`: the kernels index it up to there from the call's sizes."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call reads or writes {numel}")
 
 
 def _window_args(mode: str, window):
@@ -280,6 +300,11 @@ def paged_attn_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, mo
     shape = make_shape(q, k_pool, v_pool, block_table, S, scale, flags, split_tokens)
     _i32(seq_lens, "seq_lens")
     m, n_runs, win = _window_args(mode, window)
+    i32, f32 = torch.int32, torch.float32
+    _sized(seq_lens, "seq_lens", S, i32)
+    _sized(win, "window", S * n_runs * 2, i32)
+    _sized(out, "out", S * shape.n_q_heads * shape.head_dim, f32)
+    _sized(lse, "lse", S * shape.n_q_heads, f32)
     need = int(lib().pkv_decode_workspace_bytes(ctypes.byref(shape), m, n_runs))
     if need == 0:
         _check(lib().pkv_paged_attn_decode(ctypes.byref(shape), None, None, None, None, None, m, n_runs,
@@ -326,6 +351,13 @@ def paged_attn_prefill_window(q, cu_q, q_pos, k_pool, v_pool, block_table, seq_l
     for name, t in (("cu_q", cu_q), ("q_pos", q_pos), ("seq_lens", seq_lens)):
         _i32(t, name)
     m, n_runs, win = _window_args(mode, window)
+    i32, f32 = torch.int32, torch.float32
+    _sized(cu_q, "cu_q", S + 1, i32)
+    _sized(q_pos, "q_pos", Nq, i32)
+    _sized(seq_lens, "seq_lens", S, i32)
+    _sized(win, "window", S * n_runs * 2, i32)
+    _sized(out, "out", Nq * shape.n_q_heads * shape.head_dim, f32)
+    _sized(lse, "lse", Nq * shape.n_q_heads, f32)
     need = int(lib().pkv_prefill_workspace_bytes(ctypes.byref(shape), Nq, max_q_per_seq, m, n_runs))
     ws = _workspace(need, q, workspace) if need else workspace
     if out is None:
@@ -427,6 +459,9 @@ def kv_store(k_new, v_new, positions, k_pool, v_pool, block_table, seq_ids=None,
     if k_new.dim() != 3 or k_pool.dim() != 4:
         raise TypeError("k_new is [n_tok, n_kv_heads, head_dim]; pools are [n_blocks, n_kv_heads, block_size, W]")
     n_tok, hkv, hd = k_new.shape
+    _sized(positions, "positions", n_tok, torch.int32)
+    _sized(seq_ids, "seq_ids", n_tok, torch.int32)
+    _sized(skipped, "skipped", 1, torch.int32)
     nb, phkv, bs = k_pool.shape[:3]
     if phkv != hkv:
         raise ValueError("k_new and k_pool disagree on n_kv_heads")

@@ -274,3 +274,33 @@ def test_decode_full_size_sampled(cfg, n_sample):
     log(f"  oracle on sequences {seqs}")
     ro, rl, rows = d.oracle(seqs)
     compare(o[rows], l[rows], ro, rl, tol_of(w), f"{w.name} sampled")
+
+
+def test_binding_refuses_undersized_arguments():
+    """Outputs, lengths, windows and pools that are smaller than the call's
+    sizes say are refused before any launch."""
+    import torch
+
+    w = wgen.make_custom(seed=4, n_seqs=3, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16, ctx=(10, 60))
+    d = Dev(w)
+    S, H, hd = w.n_seqs, w.n_q_heads, w.head_dim
+    cases = [
+        dict(out=torch.empty((S, H, hd - 1), dtype=torch.float32, device="cuda")),
+        dict(out=torch.empty((S, H, hd), dtype=torch.float16, device="cuda")),
+        dict(lse=torch.empty((S, H - 1), dtype=torch.float32, device="cuda")),
+    ]
+    for kw in cases:
+        with pytest.raises((TypeError, ValueError)):
+            d.decode(**kw)
+    with pytest.raises(ValueError):
+        pkv.paged_attn_decode(d.q, d.k, d.v, d.table, d.lens[:2].contiguous(), w.scale)
+    with pytest.raises(ValueError):
+        pkv.paged_attn_decode(d.q, d.k, d.v, d.table, d.lens, w.scale, mode="span",
+                              window=torch.zeros((S - 1, 2), dtype=torch.int32, device="cuda"))
+    with pytest.raises(TypeError):
+        pkv.paged_attn_decode(d.q, d.k[..., :64].contiguous(), d.v, d.table, d.lens, w.scale)
+    with pytest.raises(TypeError):
+        pkv.paged_attn_decode(d.q[..., :64].contiguous(), d.k, d.v, d.table, d.lens, w.scale)
+    out, lse = d.decode()  # the well-formed call still works
+    ro, rl = d.oracle()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), "after refusals")
