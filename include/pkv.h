@@ -38,6 +38,12 @@
  *  - No internal locking ("Tiered KV cache — architecture", section "The
  *    single-threading contract"): one caller mutates a pool at a time;
  *    calls on one stream are ordered.
+ *  - Graph capture: the decode calls, pkv_paged_attn_prefill_window,
+ *    pkv_kv_store, pkv_cow_apply and the int4 codec only launch kernels on
+ *    `stream` (no synchronization, allocation or memset), so they can be
+ *    captured into a HIP graph and replayed.  With PKV_FLAG_CHECKED they
+ *    wait for the stream and cannot; pkv_kv_copy_cells plans on the host and
+ *    waits for its upload, so it cannot either.
  */
 #ifndef PKV_H
 #define PKV_H
