@@ -451,6 +451,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   const int32_t lim = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
   const int64_t row0 = (int64_t)s * nslot * a.n_q_heads + h;  // slot stride n_q_heads
   float m = -INFINITY, l = 0.f, acc = 0.f;
+  // slot = run * nspl + k, walked in order without dividing: (run, k) and
+  // the run's clipped range advance with the slot (same ranges as
+  // split_range gives)
+  int run = 0, k = 0;
+  int32_t rl, rh;
+  run_range(a, s, 0, lim, rl, rh);
   for (int s0 = 0; s0 < nslot; s0 += kUnroll) {
     float2 ml[kUnroll];
     float o[kUnroll];
@@ -460,12 +466,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
       ml[u] = make_float2(-INFINITY, 0.f);
       o[u] = 0.f;
       if (slot < nslot) {
-        int32_t lo, hi;
-        split_range(a, s, slot, lim, lo, hi);
+        const int64_t w0 = (int64_t)k * a.split;
+        const int64_t lo = rl > w0 ? rl : w0;
+        const int64_t hi = rh < w0 + a.split ? rh : w0 + a.split;
         if (lo < hi) {
           const int64_t r = row0 + (int64_t)slot * a.n_q_heads;
           ml[u] = *(const float2*)(a.part_ml + r * 2);
           o[u] = a.part_o[r * HD + d];
+        }
+        if (++k == a.nspl) {
+          k = 0;
+          if (++run < a.n_runs) run_range(a, s, run, lim, rl, rh);
         }
       }
     }
