@@ -11,33 +11,67 @@
 
 namespace pkv {
 
-// One work unit = one W-sized word of one row; a row is n_kv_heads segments.
+// One wave per (row, source) pair; a row is n_kv_heads segments of
+// seg_bytes, block-strided in the pool and contiguous in the stage.  The
+// lanes take the row's W-sized words in order; each lane splits its first
+// word into (segment, word) once and then steps by 64 words with a carry,
+// so no division runs per word.
 template <typename W>
 __global__ __launch_bounds__(256) void copy_rows_kernel(int phase, PoolGeom g, unsigned char* stage,
                                                         const int32_t* pairs, int32_t n_pairs) {
-  const int64_t per_seg = g.seg_bytes / (int64_t)sizeof(W);
-  const int64_t per_row = per_seg * g.n_kv_heads;
-  const int64_t total = per_row * n_pairs;
-  const int64_t head_stride = g.block_size * g.seg_bytes;
+  const int lane = threadIdx.x & 63;
+  const int32_t p = (int32_t)blockIdx.x * 4 + (int32_t)(threadIdx.x >> 6);  // wave-uniform
+  if (p >= n_pairs) return;
+  const int32_t per_seg = (int32_t)(g.seg_bytes / (int64_t)sizeof(W));
+  const int32_t per_row = per_seg * g.n_kv_heads;
+  const int64_t head_stride = (int64_t)g.block_size * g.seg_bytes;
   const int64_t block_bytes = g.n_kv_heads * head_stride;
-  const int64_t row_bytes = g.n_kv_heads * g.seg_bytes;  // a row in the stage is contiguous
-  auto pool_word = [&](int64_t row, int64_t h, int64_t c) {
-    const int64_t blk = row / g.block_size, slot = row - blk * g.block_size;
-    return (W*)(g.base + blk * block_bytes + h * head_stride + slot * g.seg_bytes) + c;
+  const int64_t row_bytes = (int64_t)g.n_kv_heads * g.seg_bytes;  // a row in the stage
+  auto pool_row = [&](int32_t row) {  // first byte of the row's segment 0 in the pool
+    const int32_t blk = row / g.block_size, slot = row - blk * g.block_size;
+    return g.base + (int64_t)blk * block_bytes + (int64_t)slot * g.seg_bytes;
   };
-  for (int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; f < total;
-       f += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t p = f / per_row, w = f - p * per_row;
-    const int64_t h = w / per_seg, c = w - h * per_seg;
-    const int32_t x = pairs[2 * p], y = pairs[2 * p + 1];
-    if (phase == 1) {
-      // x = pool row, y = stage index
-      W* dst = (W*)(stage + (int64_t)y * row_bytes) + w;
-      *dst = *pool_word(x, h, c);
+  const int32_t x = pairs[2 * p], y = pairs[2 * p + 1];
+  int32_t h = lane / per_seg, c = lane - h * per_seg;
+  const int32_t dh = 64 / per_seg, dc = 64 - dh * per_seg;
+  if (phase == 1) {
+    // x = pool row, y = stage index
+    const unsigned char* src = pool_row(x);
+    W* dst = (W*)(stage + (int64_t)y * row_bytes);
+    for (int32_t w = lane; w < per_row; w += 64) {
+      dst[w] = ((const W*)(src + h * head_stride))[c];
+      c += dc;
+      h += dh;
+      if (c >= per_seg) {
+        c -= per_seg;
+        ++h;
+      }
+    }
+  } else {
+    // x = pool row; y >= 0 pool row, y < 0 stage index -(y + 1)
+    unsigned char* dst = pool_row(x);
+    if (y >= 0) {
+      const unsigned char* src = pool_row(y);
+      for (int32_t w = lane; w < per_row; w += 64) {
+        ((W*)(dst + h * head_stride))[c] = ((const W*)(src + h * head_stride))[c];
+        c += dc;
+        h += dh;
+        if (c >= per_seg) {
+          c -= per_seg;
+          ++h;
+        }
+      }
     } else {
-      // x = pool row; y >= 0 pool row, y < 0 stage index -(y + 1)
-      const W* src = y >= 0 ? pool_word(y, h, c) : (const W*)(stage + (int64_t)(-(y + 1)) * row_bytes) + w;
-      *pool_word(x, h, c) = *src;
+      const W* src = (const W*)(stage + (int64_t)(-(y + 1)) * row_bytes);
+      for (int32_t w = lane; w < per_row; w += 64) {
+        ((W*)(dst + h * head_stride))[c] = src[w];
+        c += dc;
+        h += dh;
+        if (c >= per_seg) {
+          c -= per_seg;
+          ++h;
+        }
+      }
     }
   }
 }
@@ -122,9 +156,7 @@ hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stag
                             const int32_t* pairs, int32_t n_pairs, hipStream_t st) {
   if (n_pairs <= 0) return hipSuccess;
   const bool wide = (pool.seg_bytes % 16) == 0;
-  const int64_t units = (pool.seg_bytes / (wide ? 16 : 4)) * pool.n_kv_heads * (int64_t)n_pairs;
-  int64_t blocks = (units + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t blocks = ((int64_t)n_pairs + 3) / 4;  // one wave per pair
   if (wide)
     hipLaunchKernelGGL(copy_rows_kernel<uint4>, dim3((unsigned)blocks), dim3(256), 0, st, phase,
                        pool, stage, pairs, n_pairs);
