@@ -85,7 +85,7 @@ template <typename W>
 __global__ __launch_bounds__(256) void copy_runs_kernel(PoolGeom g, const int32_t* moves,
                                                         const int32_t* cum, int32_t n_moves,
                                                         int32_t total_rows) {
-  constexpr int kRows = 16, kUnroll = 4;
+  constexpr int kRows = 16;
   __shared__ int64_t src_off[kRows], dst_off[kRows];  // byte offset of the row's first segment
   const int64_t head_stride = g.block_size * g.seg_bytes;
   const int64_t block_bytes = g.n_kv_heads * head_stride;
@@ -109,30 +109,25 @@ __global__ __launch_bounds__(256) void copy_runs_kernel(PoolGeom g, const int32_
     dst_off[threadIdx.x] = dof;
   }
   __syncthreads();
-  const uint32_t per_seg = (uint32_t)(g.seg_bytes / (int64_t)sizeof(W));
-  const uint32_t per_row = per_seg * (uint32_t)g.n_kv_heads;
-  const uint32_t total = kRows * per_row;
-  // word f of the workgroup: row f / per_row, head h, word c of the segment
-  auto at = [&](int64_t row_off, uint32_t w) {
-    const uint32_t h = w / per_seg, c = w - h * per_seg;
-    return (W*)(g.base + row_off + h * head_stride) + c;
-  };
-  for (uint32_t f0 = threadIdx.x; f0 < total; f0 += kUnroll * blockDim.x) {
-    W v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t f = f0 + u * blockDim.x;
-      if (f < total) {
-        const uint32_t i = f / per_row;
-        if (src_off[i] >= 0) v[u] = *at(src_off[i], f - i * per_row);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t f = f0 + u * blockDim.x;
-      if (f < total) {
-        const uint32_t i = f / per_row;
-        if (dst_off[i] >= 0) *at(dst_off[i], f - i * per_row) = v[u];
+  // wave v copies rows v, v + 4, ...; its lanes walk a row's words by an
+  // incremental (segment, word) pair, so no division runs per word
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int32_t per_seg = (int32_t)(g.seg_bytes / (int64_t)sizeof(W));
+  const int32_t per_row = per_seg * g.n_kv_heads;
+  const int32_t h0 = lane / per_seg, c0 = lane - h0 * per_seg;
+  const int32_t dh = 64 / per_seg, dc = 64 - dh * per_seg;
+  for (int i = wv; i < kRows; i += 4) {
+    const int64_t so = src_off[i], dof = dst_off[i];
+    if (so < 0) continue;  // past the last row (wave-uniform)
+    int32_t h = h0, c = c0;
+    for (int32_t w = lane; w < per_row; w += 64) {
+      const int64_t off = h * head_stride + (int64_t)c * (int64_t)sizeof(W);
+      *(W*)(g.base + dof + off) = *(const W*)(g.base + so + off);
+      c += dc;
+      h += dh;
+      if (c >= per_seg) {
+        c -= per_seg;
+        ++h;
       }
     }
   }
