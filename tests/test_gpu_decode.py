@@ -304,3 +304,35 @@ def test_binding_refuses_undersized_arguments():
     out, lse = d.decode()  # the well-formed call still works
     ro, rl = d.oracle()
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), "after refusals")
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_kv_map_at_the_run_limit(kind):
+    """Eight runs per sequence (the most a kv_map may hold; runs overlap, stick
+    out of the sequence or are empty) through decode, prefill and the
+    resolver against the oracle; nine runs are refused."""
+    import torch
+
+    w = wgen.make_custom(seed=88, n_seqs=7, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
+                         fmts=("f16", "q8_0", "f16"), ctx=(1, 800), mode="kv_map", n_runs=8, kind=kind,
+                         hole_frac=0.1)
+    assert w.kv_map.shape[1] == 8
+    d = Dev(w)
+    out, lse = d.decode() if kind == "decode" else d.prefill()
+    ro, rl = d.oracle()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), f"{kind} 8 runs")
+    n_cand = int(np.max(np.sum(np.maximum(w.kv_map[:, :, 1], 0), axis=1))) + 3
+    kw = {} if kind == "decode" else dict(cu_q=d.cu_q, q_pos=d.q_pos)
+    rows = pkv.resolve_rows(d.table, d.lens, w.block_size, w.n_kv_heads, w.head_dim, w.n_pool_blocks, n_cand,
+                            mode="kv_map", window=d.window, k_fmt=pkv.Q8_0, **kw)
+    qs, qp = (np.arange(w.n_seqs), w.seq_lens - 1) if kind == "decode" else (w.q_seq(), w.q_pos)
+    ref = oracle.resolve_rows("kv_map", w.block_table, w.seq_lens, w.block_size, qs, qp, n_cand, w.window,
+                              w.kv_map)
+    assert np.array_equal(rows.cpu().numpy(), ref)
+    nine = torch.zeros((w.n_seqs, 9, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError):
+        if kind == "decode":
+            pkv.paged_attn_decode(d.q, d.k, d.v, d.table, d.lens, w.scale, mode="kv_map", window=nine)
+        else:
+            pkv.paged_attn_prefill_window(d.q, d.cu_q, d.q_pos, d.k, d.v, d.table, d.lens, w.scale,
+                                          int(np.max(np.diff(w.cu_q))), mode="kv_map", window=nine)
