@@ -132,3 +132,20 @@ def test_prefill_workload4_full_size_sampled():
     seqs = [0, 5, 8, 13]  # two span-style and two multi-run sequences
     ro, rl, rows = d.oracle(seqs)
     compare(o[rows], l[rows], ro, rl, tol_of(w), "w4 full sampled")
+
+
+def test_prefill_more_sequences_than_the_order_sort_holds():
+    """4,100 short sequences: more than the order kernel sorts (4,096), so
+    the sequences keep their own order; results still match the oracle, and
+    decode over the same batch does too."""
+    w = wgen.make_custom(seed=41, n_seqs=4100, n_q_heads=4, n_kv_heads=2, head_dim=64, block_size=16,
+                         ctx=(1, 40), mode="kv_map", n_runs=2, kind="prefill", q_per_seq=(1, 3), hole_frac=0.0)
+    d = Dev(w)
+    out, lse = d.prefill()
+    ro, rl = d.oracle()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), "4100 seqs prefill")
+    w.kind, w.cu_q, w.q_pos = "decode", None, None
+    d = Dev(w)
+    out, lse = d.decode()
+    ro, rl = d.oracle()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), "4100 seqs decode")
