@@ -322,6 +322,8 @@ def run_decode(cfg, args):
         "queries_per_s": round(w.n_seqs / (ms * 1e-3), 1),
         "hbm_frac_uniq_step": round(b_uniq_kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "event_ms": {"step_median": round(float(np.median(step_ms)), 5),
+                     "step_p10": round(float(np.percentile(step_ms, 10)), 5),
+                     "step_p90": round(float(np.percentile(step_ms, 90)), 5),
                      "split_avg": round(split_avg_ms, 5),
                      "merge_avg": round(float(np.mean(merge_ms)), 5)},
         "roofline": {
@@ -413,6 +415,8 @@ def run_prefill(args):
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": stored_traffic("prefill4"), "hbm_GBps": round(io_bytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "event_ms": {"median": round(float(np.median(times)), 5), "p10": round(float(np.percentile(times, 10)), 5),
+                     "p90": round(float(np.percentile(times, 90)), 5)},
     }
 
 
