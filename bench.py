@@ -399,6 +399,14 @@ def run_prefill(args):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     ms = float(np.mean(times))
+    # warm figure, labelled: the same calls back to back, inputs left in the caches
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(args.steps):
+        call()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
     flops, kv_bytes, pairs = prefill_work(w, dev)
     tflops = flops / (ms * 1e-3) / 1e12
     io_bytes = kv_bytes + q.numel() * 2 + out.numel() * 4 + lse.numel() * 4
@@ -417,6 +425,8 @@ def run_prefill(args):
                      "hbm_frac": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "event_ms": {"median": round(float(np.median(times)), 5), "p10": round(float(np.percentile(times, 10)), 5),
                      "p90": round(float(np.percentile(times, 90)), 5)},
+        "warm_unflushed": {"ms_per_call": round(warm_ms, 5),
+                           "TFLOPs": round(flops / (warm_ms * 1e-3) / 1e12, 2)},
     }
 
 
