@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kI4Threads) void int4_encode_kernel(Int4Args a) {
   // x / scale, so rint(t) is the code unless t lies within 2^-18 of a
   // half-integer (then RN(x / scale) could sit on the other side of it, or
   // on it); those elements, and blocks whose scale is extreme, take the
-  // division.  |t - rint(t)| and its distance to 1/2 are exact in binary32.
+  // division.  t - rint(t) is exact in binary32 and at most 1/2 in size, so
+  // "within 2^-18 of a half-integer" is |t - rint(t)| >= 1/2 - 2^-18.
   const bool fast = scale >= 0x1p-100f && scale <= 0x1p+100f;
   const float r = 1.0f / scale;
 #pragma unroll
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kI4Threads) void int4_encode_kernel(Int4Args a) {
         const float x = g[c].at(i);
         const float tq = x * r;
         q[i] = rintf(tq);
-        slow |= fabsf(fabsf(tq - q[i]) - 0.5f) <= 0x1p-18f;
+        slow |= fabsf(tq - q[i]) >= 0.5f - 0x1p-18f;  // within 2^-18 of a half-integer
       }
       if (slow) {  // rare: redo the group with the division
 #pragma unroll

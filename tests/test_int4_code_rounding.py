@@ -2,7 +2,8 @@
 
 The encoder computes code = rint(x / scale) (binary32 division) as
 rint(RN(x * RN(1 / scale))) and falls back to the division when that product
-lies within 2^-18 of a half-integer.  This replays exactly that arithmetic in
+lies within 2^-18 of a half-integer (|t - rint(t)| >= 1/2 - 2^-18).  This
+replays exactly that arithmetic in
 numpy float32 on values packed around every code boundary, at scales from
 2^-100 to 2^100, and requires it to equal division-then-rint everywhere; the
 same values without the fallback must show mismatches (so the fallback is
@@ -33,7 +34,7 @@ def test_fast_rounding_equals_division():
         want = np.rint(x / scale)
         t = (x * r).astype(F32)
         q = np.rint(t)
-        near = np.abs(np.abs(t - q) - F32(0.5)) <= F32(2.0 ** -18)
+        near = np.abs(t - q) >= F32(0.5) - F32(2.0 ** -18)  # the kernel's form of the test
         assert np.array_equal(np.where(near, want, q), want)
         unguarded_mismatches += int(np.sum(q != want))
     assert unguarded_mismatches > 0
