@@ -136,11 +136,14 @@ __global__ __launch_bounds__(kI4Threads) void int4_encode_kernel(Int4Args a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = rintf(g[c].at(i) / scale);
       }
+      // code + 8 (1..15) is the low nibble of the binary32 2^23 + 8 + code;
+      // xor 8 turns it into the code's 4-bit two's complement
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int code = (int)fminf(fmaxf(q[i], -7.f), 7.f);
-        word |= (uint32_t)(code & 0xF) << (4 * i);
+        const uint32_t bits = __builtin_bit_cast(uint32_t, fminf(fmaxf(q[i], -7.f), 7.f) + 8388616.0f);
+        word |= (bits & 0xFu) << (4 * i);
       }
+      word ^= 0x88888888u;
     }
     *(uint32_t*)(blob + 4 + gi * 4) = word;
   }
