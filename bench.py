@@ -329,6 +329,9 @@ def run_decode(cfg, args):
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_split_kernel",
+            # the events bracket the partials call: the one-workgroup plan
+            # kernel (when the call is planned) and the split kernel
+            "timed": "decode partials call (decode_plan_kernel + decode_split_kernel)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -131,9 +131,14 @@ int64_t pkv_row_bytes(int32_t fmt, int32_t n_kv_heads, int32_t head_dim);
  * section "Problem": a decode step dots the new query against the stored
  * history).  Split-K: each (sequence, kv head, split of the window) is a
  * separate work item producing (max, sum, unnormalised output); a second
- * pass merges the splits by log-sum-exp.  The split size depends only on
- * the shape, so results are deterministic and do not change when blocks
- * move in the pool and the table follows.
+ * pass merges the splits by log-sum-exp.  Calls with many possible items
+ * first list the non-empty ones on the device (a one-workgroup plan pass)
+ * and cut each sequence's last few full splits into shorter pieces, so the
+ * split pass ends on short items.  The split size depends only on the
+ * shape, and which splits are cut only on the shape and the sequence's own
+ * length and window, so results are deterministic, do not depend on the
+ * other sequences' lengths, and do not change when blocks move in the pool
+ * and the table follows.
  *
  * q:   [n_seqs][n_q_heads][head_dim] in q_fmt.
  * out: float32 [n_seqs][n_q_heads][head_dim] = sum_t w_t v_t / sum_t w_t.

@@ -3,14 +3,12 @@
 
 namespace pkv {
 
-hipError_t launch_decode_split_f32(const AttnArgs& a, int hd, int bs, int g, hipStream_t st,
-                                     bool* found) {
-  const dim3 grid(a.n_kv_heads, a.n_runs * a.nspl, a.n_seqs);
-#define PKV_CASE(HD, BS, G)                                                                \
-  if (hd == HD && bs == BS && g == G) {                                                    \
-    hipLaunchKernelGGL((decode_split_kernel<HD, BS, G, kComboF32>), grid, dim3(64), 0, st, a); \
-    *found = true;                                                                         \
-    return hipGetLastError();                                                              \
+hipError_t launch_decode_split_f32(const AttnArgs& a, int hd, int bs, int g, int64_t max_units,
+                                     hipStream_t st, bool* found) {
+#define PKV_CASE(HD, BS, G)                                                  \
+  if (hd == HD && bs == BS && g == G) {                                      \
+    *found = true;                                                           \
+    return launch_split_instance<HD, BS, G, kComboF32>(a, max_units, st);      \
   }
 #define PKV_CASES_G(HD, BS) PKV_CASE(HD, BS, 1) PKV_CASE(HD, BS, 2) PKV_CASE(HD, BS, 3) PKV_CASE(HD, BS, 4) PKV_CASE(HD, BS, 8)
   PKV_CASES_G(64, 16)

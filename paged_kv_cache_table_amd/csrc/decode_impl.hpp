@@ -6,9 +6,14 @@
 // the positions of its window that lie in [0, seq_len) and are not in a
 // hole, reading K/V rows through the block table.
 //
-// Work item = one wave = (sequence, kv head, split slot).  A split slot is
-// the intersection of one window run with an aligned range of `split`
-// positions, so its blocks are at most 64 and their ids fit one register.
+// Work unit = (item, kv head), one wave at a time.  An item is a split slot
+// (the intersection of one window run with an aligned range of `split`
+// positions, so its blocks are at most 64 and their ids fit one register)
+// or a piece of one.  For calls with many possible items the plan pass
+// lists them without gaps: whole slots first, the pieces of cut slots
+// last, so the hardware dispatcher keeps every wave slot busy and the pass
+// ends on short units.  Smaller calls skip the plan and launch one
+// workgroup per possible slot.
 // Lane layout: each token row of one kv head is spread over LPT = HD/16
 // lanes (16 elements per lane), a pass covers TPP = 64/LPT tokens, and a
 // 16- or 32-token block takes BS/TPP passes.  The g query heads that share
@@ -260,28 +265,48 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
   constexpr int RING = kRingFit < 2 ? 2 : (kRingFit > 8 ? 8 : kRingFit);
   constexpr float kEmpty = -1e30f;  // running max before any visible token
 
-  // kv head is the fastest grid index: the Hkv waves that read interleaved
-  // slices of the same pool rows are dispatched together.
-  const int kvh = blockIdx.x, slot = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x, tok = lane / LPT, sub = lane % LPT;
-  const int32_t L = clamp_seq_len(a.seq_lens[s], a.max_blocks, BS);
+  // Planned calls: one workgroup per unit of the list, units item-major
+  // (kv head fastest: the Hkv waves that read interleaved slices of the
+  // same pool rows start together); the grid is the host's bound on units
+  // and the workgroups past the count the plan wrote, all at the end of the
+  // grid, leave at once.  Direct calls: grid (kv head, slot, sequence),
+  // empty slots leave at once.
+  int s, kvh;
   int32_t lo, hi;
-  split_range(a, s, slot, L, lo, hi);
-  if (lo >= hi) return;  // this slot is not a work item
+  int64_t prow;
+  if (a.items) {
+    const uint32_t unit = blockIdx.x;
+    if (unit >= a.hdr[0]) return;
+    const uint32_t item = unit / (uint32_t)a.n_kv_heads;
+    kvh = (int)(unit - item * (uint32_t)a.n_kv_heads);
+    const uint4 it = a.items[item];  // (sequence, lo, hi, partial row), lo < hi
+    s = (int)__builtin_amdgcn_readfirstlane((int)it.x);
+    lo = __builtin_amdgcn_readfirstlane((int)it.y);
+    hi = __builtin_amdgcn_readfirstlane((int)it.z);
+    prow = (uint32_t)__builtin_amdgcn_readfirstlane((int)it.w);
+  } else {
+    kvh = blockIdx.x;
+    const int slot = blockIdx.y;
+    s = blockIdx.z;
+    split_range(a, s, slot, clamp_seq_len(a.seq_lens[s], a.max_blocks, BS), lo, hi);
+    if (lo >= hi) return;  // not a work item
+    prow = (int64_t)s * a.rows_per_seq + slot;
+  }
 
   const int32_t jb0 = lo / BS;
   const int32_t nblk = (hi - 1) / BS - jb0 + 1;  // <= 64 by construction
   int32_t myid = -1;
   if (lane < nblk) myid = block_id(a, s, jb0 + lane, kvh == 0);
+  // q is read while the block ids are in flight
+  KP kp;
+  const int64_t qoff = ((int64_t)s * a.n_q_heads + (int64_t)kvh * G) * HD;
+  kp.load_q((const QT*)a.q + qoff, sub);
   // The ballot is wave-uniform; readfirstlane makes that visible to the
   // compiler, so loops over it stay scalar (no exec-masked flow blocks).
   const uint64_t bal = __ballot(myid >= 0);
   const uint64_t mask = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(bal >> 32)) << 32) |
                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bal);
-
-  KP kp;
-  const int64_t qoff = ((int64_t)s * a.n_q_heads + (int64_t)kvh * G) * HD;
-  kp.load_q((const QT*)a.q + qoff, sub);
 
   // m: running max of the scaled scores (log2 domain), wave-uniform; l and
   // acc: this lane's running sum and output for its tokens, all relative to m.
@@ -407,8 +432,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e]);
   }
-  const int nslot = a.n_runs * a.nspl;
-  const int64_t base = ((int64_t)s * nslot + slot) * a.n_q_heads + (int64_t)kvh * G;
+  const int64_t base = prow * a.n_q_heads + (int64_t)kvh * G;
   if (tok == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -433,13 +457,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split slots of each (sequence, q head) by log-sum-exp:
+// Launch of one split kernel instance: planned, one one-wave workgroup per
+// unit the call can have at most (max_units); direct, grid (kv head, slot,
+// sequence).
+template <int HD, int BS, int G, int COMBO>
+hipError_t launch_split_instance(const AttnArgs& a, int64_t max_units, hipStream_t st) {
+  const dim3 grid = a.items ? dim3((unsigned)max_units)
+                            : dim3((unsigned)a.n_kv_heads, (unsigned)(a.n_runs * a.nspl), (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((decode_split_kernel<HD, BS, G, COMBO>), grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+// Merge the partials of each (sequence, q head) by log-sum-exp:
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, lse = (M + log2 L) ln 2.
 // One workgroup per (256 consecutive (q head, dim) outputs, sequence): each
-// thread owns one output and merges the slots in slot order with a running
-// max (rescaling when it grows), so a single pass suffices; the partial
-// loads of eight slots are issued before their arithmetic.  The merge order
-// is fixed, so results are deterministic.
+// thread owns one output and merges the partials in a fixed order (slot
+// order; a cut slot's own row, then its pieces) with a running max,
+// rescaling when it grows, so a single pass suffices and results are
+// deterministic; the loads of eight rows are issued before their
+// arithmetic.  Which slots exist, and which are cut, follows from the
+// sequence's own length and window, exactly as the plan pass decides.
 template <int HD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   constexpr int kUnroll = 8;
@@ -447,47 +484,52 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   const int idx = blockIdx.x * 256 + threadIdx.x;  // q head * HD + dim
   if (idx >= a.n_q_heads * HD) return;
   const int h = idx / HD, d = idx - h * HD;
-  const int nslot = a.n_runs * a.nspl;
   const int32_t lim = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
-  const int64_t row0 = (int64_t)s * nslot * a.n_q_heads + h;  // slot stride n_q_heads
-  float m = -INFINITY, l = 0.f, acc = 0.f;
-  // slot = run * nspl + k, walked in order without dividing: (run, k) and
-  // the run's clipped range advance with the slot (same ranges as
-  // split_range gives)
-  int run = 0, k = 0;
   int32_t rl, rh;
-  run_range(a, s, 0, lim, rl, rh);
-  for (int s0 = 0; s0 < nslot; s0 += kUnroll) {
-    float2 ml[kUnroll];
-    float o[kUnroll];
+  int nfull = 0;
+  for (int r = 0; r < a.n_runs; ++r) {
+    run_range(a, s, r, lim, rl, rh);
+    nfull += full_slots(rl, rh, a.split);
+  }
+  const int first_cut = nfull - (nfull < a.fine_per_seq ? nfull : a.fine_per_seq);
+  float m = -INFINITY, l = 0.f, acc = 0.f;
+  auto add = [&](float2 ml, float o) {
+    if (ml.x == -INFINITY) return;  // a partial that saw nothing carries no weight
+    const float mn = fmaxf(m, ml.x);
+    const float ca = fast_exp2(m - mn), cb = fast_exp2(ml.x - mn);  // m = -inf -> ca = 0
+    acc = acc * ca + cb * o;
+    l = l * ca + cb * ml.y;
+    m = mn;
+  };
+  // A run's non-empty slots k0..k1, each followed by its pieces when cut,
+  // hold one contiguous range of rows: row(slot) = slot + (cut slots
+  // before it) * (nsub - 1).
+  int full_before = 0;
+  for (int r = 0; r < a.n_runs; ++r) {
+    run_range(a, s, r, lim, rl, rh);
+    if (rh <= rl) continue;
+    const int nf = full_slots(rl, rh, a.split);
+    const int k0 = rl / a.split, k1 = (rh - 1) / a.split;
+    const int cut0 = full_before > first_cut ? full_before - first_cut : 0;
+    const int cut1 = full_before + nf > first_cut ? full_before + nf - first_cut : 0;
+    full_before += nf;
+    const int64_t row_a = (int64_t)s * a.rows_per_seq + (int64_t)r * a.nspl + k0 + (int64_t)cut0 * (a.nsub - 1);
+    const int n_rows = k1 - k0 + 1 + (cut1 - cut0) * (a.nsub - 1);
+    for (int i0 = 0; i0 < n_rows; i0 += kUnroll) {
+      float2 ml[kUnroll];
+      float o[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int slot = s0 + u;
-      ml[u] = make_float2(-INFINITY, 0.f);
-      o[u] = 0.f;
-      if (slot < nslot) {
-        const int64_t w0 = (int64_t)k * a.split;
-        const int64_t lo = rl > w0 ? rl : w0;
-        const int64_t hi = rh < w0 + a.split ? rh : w0 + a.split;
-        if (lo < hi) {
-          const int64_t r = row0 + (int64_t)slot * a.n_q_heads;
-          ml[u] = *(const float2*)(a.part_ml + r * 2);
-          o[u] = a.part_o[r * HD + d];
-        }
-        if (++k == a.nspl) {
-          k = 0;
-          if (++run < a.n_runs) run_range(a, s, run, lim, rl, rh);
+      for (int u = 0; u < kUnroll; ++u) {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        o[u] = 0.f;
+        if (i0 + u < n_rows) {
+          const int64_t row = (row_a + i0 + u) * a.n_q_heads + h;
+          ml[u] = *(const float2*)(a.part_ml + row * 2);
+          o[u] = a.part_o[row * HD + d];
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (ml[u].x == -INFINITY) continue;  // a slot that saw nothing carries no weight
-      const float mn = fmaxf(m, ml[u].x);
-      const float ca = fast_exp2(m - mn), cb = fast_exp2(ml[u].x - mn);  // m = -inf -> ca = 0
-      acc = acc * ca + cb * o[u];
-      l = l * ca + cb * ml[u].y;
-      m = mn;
+      for (int u = 0; u < kUnroll; ++u) add(ml[u], o[u]);
     }
   }
   const int64_t oi = ((int64_t)s * a.n_q_heads + h) * HD + d;

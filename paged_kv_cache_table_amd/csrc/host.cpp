@@ -82,7 +82,13 @@ int combo_of(int qf, int kf, int vf) {
 
 struct Plan {
   int combo = -1, g = 0, runs = 1, split = 0, nspl = 0;
-  size_t off_o = 0, off_ml = 0, off_err = 0, total = 0;
+  // decode: whether the call runs the plan pass, pieces per cut slot, their
+  // size, cut slots per sequence, partial rows per sequence and the most
+  // items a call can have
+  bool planned = false;
+  int nsub = 1, fine = 0, fine_per_seq = 0;
+  int64_t rows_per_seq = 0, max_items = 0;
+  size_t off_o = 0, off_ml = 0, off_err = 0, off_items = 0, off_seq = 0, off_hdr = 0, total = 0;
 };
 
 // Validation shared by every attention call.
@@ -170,10 +176,40 @@ pkv_status plan_decode(const pkv_shape* sh, int mode, int n_runs, const void* wi
                 (long long)(nspl * P->runs), sh->max_blocks_per_seq, sh->block_size, split, P->runs);
   P->split = split;
   P->nspl = (int)nspl;
-  const size_t slots = (size_t)sh->n_seqs * nspl * P->runs * sh->n_q_heads;
+  // Calls that can have more than four rounds of units for the device's
+  // wave slots (taken as 2048) run the plan pass: the items without gaps,
+  // ending on short units, for which each sequence cuts its last few full
+  // slots into pieces of >= 256 positions, about two rounds' worth of
+  // pieces over the whole batch (at most kMaxCutPerSeq per sequence).
+  // Smaller calls launch one workgroup per possible slot: there the plan
+  // pass would cost more than it saves.
+  constexpr int64_t kPlanMinUnits = 4 * 2048, kCutWaves = 4096, kMaxCutPerSeq = 2;
+  const int64_t slots_per_seq = nspl * P->runs;
+  P->planned = (int64_t)sh->n_seqs * slots_per_seq * sh->n_kv_heads > kPlanMinUnits;
+  P->nsub = split / 256 < 1 ? 1 : (split / 256 > 4 ? 4 : split / 256);
+  P->fine = (int)(((split + P->nsub - 1) / P->nsub + sh->block_size - 1) / sh->block_size * sh->block_size);
+  while (P->nsub > 1 && (int64_t)(P->nsub - 1) * P->fine >= split) --P->nsub;
+  P->fine_per_seq = 0;
+  if (P->planned && P->nsub > 1) {
+    const int64_t per = (int64_t)P->nsub * sh->n_kv_heads * sh->n_seqs;
+    int64_t m = (kCutWaves + per - 1) / per;
+    if (m > kMaxCutPerSeq) m = kMaxCutPerSeq;
+    P->fine_per_seq = (int)(m < slots_per_seq ? m : slots_per_seq);
+  }
+  P->rows_per_seq = slots_per_seq + (int64_t)P->fine_per_seq * (P->nsub - 1);
+  const int64_t rows = (int64_t)sh->n_seqs * P->rows_per_seq;
+  P->max_items = rows;
+  if (rows >= ((int64_t)1 << 32) || P->max_items * sh->n_kv_heads >= ((int64_t)1 << 31))
+    return fail(PKV_E_UNSUPPORTED,
+                "%lld decode work items x %d kv heads exceed the 32-bit counters; use a larger split_tokens",
+                (long long)P->max_items, sh->n_kv_heads);
+  const size_t slots = (size_t)rows * sh->n_q_heads;
   P->off_o = 0;
   P->off_ml = align_up(slots * sh->head_dim * sizeof(float), 256);
-  P->off_err = P->off_ml + align_up(slots * 2 * sizeof(float), 256);
+  P->off_items = P->off_ml + align_up(slots * 2 * sizeof(float), 256);
+  P->off_seq = P->off_items + align_up((size_t)P->max_items * 16, 256);
+  P->off_hdr = P->off_seq + align_up((size_t)sh->n_seqs * 16, 256);
+  P->off_err = P->off_hdr + 256;
   P->total = P->off_err + 256;
   return PKV_OK;
 }
@@ -246,6 +282,13 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
   a.part_o = (float*)((char*)ws + P.off_o);
   a.part_ml = (float*)((char*)ws + P.off_ml);
   a.err = (int32_t*)((char*)ws + P.off_err);
+  a.items = P.planned ? (const uint4*)((char*)ws + P.off_items) : nullptr;
+  a.hdr = (uint32_t*)((char*)ws + P.off_hdr);
+  a.nsub = P.nsub;
+  a.fine_tokens = P.fine;
+  a.fine_per_seq = P.fine_per_seq;
+  a.rows_per_seq = P.rows_per_seq;
+  a.seqinfo = (uint4*)((char*)ws + P.off_seq);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (part != kMerge) {
@@ -253,8 +296,13 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
       e = pkv::launch_zero_words(a.err, 1, s);
       if (e != hipSuccess) return device_fail(e, "clearing the error word");
     }
+    if (P.planned) {
+      e = pkv::launch_decode_plan(a, s);
+      if (e != hipSuccess) return device_fail(e, "decode plan launch");
+    }
     bool found = false;
-    e = pkv::launch_decode_split(a, P.combo, sh->head_dim, sh->block_size, P.g, s, &found);
+    e = pkv::launch_decode_split(a, P.combo, sh->head_dim, sh->block_size, P.g,
+                                 P.max_items * sh->n_kv_heads, s, &found);
     if (!found)
       return fail(PKV_E_UNSUPPORTED, "no decode kernel for head_dim %d block %d group %d",
                   sh->head_dim, sh->block_size, P.g);

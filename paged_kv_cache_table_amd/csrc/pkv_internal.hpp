@@ -27,12 +27,24 @@ struct AttnArgs {
   const int32_t* q_pos;     // prefill [n_q_total]
   float* out;
   float* lse;
-  float* part_o;   // decode partials [S][n_slots][Hq][HD]; prefill [Nq][Hq][nch][HD]
-  float* part_ml;  // decode partials [S][n_slots][Hq][2] = (max, sum); prefill [Nq][Hq][nch][2]
+  float* part_o;   // decode partials [S][rows_per_seq][Hq][HD]; prefill [Nq][Hq][nch][HD]
+  float* part_ml;  // decode partials [S][rows_per_seq][Hq][2] = (max, sum); prefill [Nq][Hq][nch][2]
   int32_t* err;    // checked mode: count of bad block ids
   int32_t n_seqs, n_q_heads, n_kv_heads, n_pool_blocks, max_blocks, block_size;
   int32_t mode, n_runs;  // n_runs = runs per sequence (1 unless kv_map)
   int32_t split, nspl;   // decode: tokens per split, split slots per run
+  // Decode work list (written by the plan pass): items [n][4] = (sequence,
+  // lo, hi, partial row); hdr[0] = units (items x kv heads); seqinfo [S][4]
+  // = the sequence's first place in each group of the list and its number
+  // of whole full slots.  A sequence's last fine_per_seq full slots are cut
+  // into nsub pieces of fine_tokens positions.  A sequence's partial rows
+  // follow its slots in order, a cut slot's pieces right after it, so the
+  // row of (slot, piece p) is slot + (cut slots before it) * (nsub - 1) + p.
+  const uint4* items;
+  uint32_t* hdr;
+  uint4* seqinfo;
+  int32_t nsub, fine_tokens, fine_per_seq;
+  int64_t rows_per_seq;
   int32_t n_q_total, max_q;
   int32_t nch;           // prefill: chunks each workgroup's window is split into
   // Pool layout [n_blocks][n_kv_heads][block_size][seg]: seg = bytes of one
@@ -93,6 +105,13 @@ __device__ inline void split_range(const AttnArgs& a, int s, int slot, int32_t l
   if (x1 < x0) x1 = x0;
   lo = (int32_t)x0;
   hi = (int32_t)x1;
+}
+
+// Number of split slots of a run [rl, rh) that it covers completely.
+__host__ __device__ inline int32_t full_slots(int32_t rl, int32_t rh, int32_t split) {
+  if (rh <= rl) return 0;
+  const int32_t k0 = (int32_t)(((int64_t)rl + split - 1) / split), k1 = rh / split;
+  return k1 > k0 ? k1 - k0 : 0;
 }
 
 // Physical block of logical block b, or -1 for a hole; ids outside
@@ -186,9 +205,11 @@ __device__ __forceinline__ float h2f_hi(uint32_t w) {
 // ---------------------------------------------------------------------------
 // Launchers (defined in the .hip files).
 
-// Decode split pass: grid (n_kv_heads, n_runs * nspl, n_seqs), 64 threads.
-hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int g, hipStream_t st,
-                               bool* found);
+// Decode plan pass (one workgroup): the work list and the unit count.
+hipError_t launch_decode_plan(const AttnArgs& a, hipStream_t st);
+// Decode split pass: grid max_units (the host's bound on units) x 64 threads.
+hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int g,
+                               int64_t max_units, hipStream_t st, bool* found);
 // Decode merge pass: grid (ceil(n_q_heads * head_dim / 256), n_seqs), 256 threads.
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
 // Prefill: workspace bytes a call needs (a multiple of 256, the last 256

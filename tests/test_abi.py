@@ -131,12 +131,28 @@ def test_decode_workspace_size_formula():
     sh = _shape(n_seqs=64, n_q_heads=32, n_kv_heads=8, max_blocks_per_seq=2048, split_tokens=512)
     assert pkv.decode_split_tokens(_shape(n_seqs=64, n_q_heads=32, n_kv_heads=8, max_blocks_per_seq=2048)) == 1024
     assert pkv.decode_split_tokens(_shape(n_seqs=32, n_q_heads=9, n_kv_heads=3, head_dim=64, max_blocks_per_seq=512)) == 256
-    nspl = 2048 * 16 // 512
-    slots = 64 * nspl * 32
     def up(x):
         return (x + 255) // 256 * 256
-    assert pkv.decode_workspace_bytes(sh) == up(slots * 128 * 4) + up(slots * 2 * 4) + 256
-    assert pkv.decode_workspace_bytes(sh, "kv_map", 4) == up(4 * slots * 128 * 4) + up(4 * slots * 2 * 4) + 256
+
+    def need(runs):
+        # partial rows: one per split slot, plus the extra pieces of the cut
+        # slots (a planned call: 64 x 64 slots x 8 kv heads > 8192 units;
+        # 512-position splits -> 2 pieces of 256; cut slots per sequence =
+        # ceil(4096 / (2 pieces x 8 kv heads x 64 seqs)) = 4, capped at 2);
+        # then the work list (16 bytes per item, at most one per row), 16
+        # bytes per sequence for its places in the list, the unit count and
+        # the error word
+        nspl = 2048 * 16 // 512
+        rows = 64 * nspl * runs + 64 * 2 * (2 - 1)
+        return up(rows * 32 * 128 * 4) + up(rows * 32 * 2 * 4) + up(rows * 16) + up(64 * 16) + 256 + 256
+
+    assert pkv.decode_workspace_bytes(sh) == need(1)
+    assert pkv.decode_workspace_bytes(sh, "kv_map", 4) == need(4)
+    # a call with at most 8192 units (4 x 32 slots x 8 kv heads here) skips
+    # the plan and cuts nothing: one row per slot
+    small = _shape(n_seqs=4, n_q_heads=32, n_kv_heads=8, max_blocks_per_seq=2048, split_tokens=1024)
+    rows = 4 * 32
+    assert pkv.decode_workspace_bytes(small) == up(rows * 32 * 128 * 4) + up(rows * 32 * 2 * 4) + up(rows * 16) + up(4 * 16) + 512
 
 
 def test_copy_cells_refuses_out_of_range_moves():

@@ -81,6 +81,42 @@ def test_decode_split_sizes(split):
     compare(out, lse, ro, rl, tol_of(w), f"split {split}")
 
 
+@pytest.mark.parametrize("mode,fmts", [
+    ("causal", ("f16", "f16", "f16")), ("causal", ("f16", "q8_0", "f16")), ("causal", ("f32", "f32", "f32")),
+    ("span", ("f16", "f16", "f16")), ("span", ("f16", "q8_0", "f16")), ("span", ("f32", "f32", "f32")),
+    ("kv_map", ("f16", "f16", "f16")), ("kv_map", ("f16", "q8_0", "f16")), ("kv_map", ("f32", "f32", "f32")),
+    ("degenerate", ("f16", "f16", "f16"))])
+def test_decode_cut_slots(mode, fmts):
+    """A planned call (64 sequences x 32 possible 1024-position slots x 8 kv
+    heads > 8192 units): the work list skips the empty slots, and each
+    sequence's last two full slots are cut into four 256-position pieces
+    (ceil(4096 / (4 x 8 x 64)) = 2), next to whole and partial slots, holes
+    and windows; "degenerate" adds empty sequences, windows and tables.
+    Against the oracle; the fused call equals partials + merge on a
+    workspace full of garbage."""
+    import torch
+
+    wmode = "kv_map" if mode == "degenerate" else mode
+    w = wgen.make_custom(seed=77, n_seqs=64, n_q_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                         fmts=fmts, ctx=(1500, 6000), mode=wmode, n_runs=3, max_blocks=2048)
+    if mode == "degenerate":
+        w.seq_lens[0] = 0                 # empty sequence
+        w.kv_map[1] = 0                   # no runs
+        w.block_table[2, :] = -1          # all holes
+        w.kv_map[3, :, 1] = -4            # negative lengths: unused runs
+    log(f"decode cut slots {mode} {fmts}")
+    d = Dev(w)
+    n_runs = 1 if wmode != "kv_map" else w.kv_map.shape[1]
+    shape = pkv.make_shape(d.q, d.k, d.v, d.table, w.n_seqs, w.scale, 0, 1024)
+    ws = torch.full((pkv.decode_workspace_bytes(shape, wmode, n_runs),), 0xAB, dtype=torch.uint8, device="cuda")
+    out, lse = d.decode(split_tokens=1024, workspace=ws)
+    d.decode(split_tokens=1024, part="partials", workspace=ws)
+    out2, lse2 = d.decode(split_tokens=1024, part="merge", workspace=ws)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    ro, rl = d.oracle()
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), f"cut {mode} {fmts}")
+
+
 @pytest.mark.parametrize("case", ["w3", "kv_map_holes", "degenerate"])
 def test_one_call_equals_partials_then_merge(case):
     """One call equals the two-call route (partials, then merge) bit for bit,
