@@ -85,20 +85,22 @@ def test_decode_split_sizes(split):
     ("causal", ("f16", "f16", "f16")), ("causal", ("f16", "q8_0", "f16")), ("causal", ("f32", "f32", "f32")),
     ("span", ("f16", "f16", "f16")), ("span", ("f16", "q8_0", "f16")), ("span", ("f32", "f32", "f32")),
     ("kv_map", ("f16", "f16", "f16")), ("kv_map", ("f16", "q8_0", "f16")), ("kv_map", ("f32", "f32", "f32")),
-    ("degenerate", ("f16", "f16", "f16"))])
+    ("kv_map8", ("f16", "f16", "f16")), ("degenerate", ("f16", "f16", "f16"))])
 def test_decode_cut_slots(mode, fmts):
     """A planned call (64 sequences x 32 possible 1024-position slots x 8 kv
     heads > 8192 units): the work list skips the empty slots, and each
     sequence's last two full slots are cut into four 256-position pieces
     (ceil(4096 / (4 x 8 x 64)) = 2), next to whole and partial slots, holes
-    and windows; "degenerate" adds empty sequences, windows and tables.
+    and windows; "kv_map8" uses the most runs a kv_map may have, and
+    "degenerate" adds empty sequences, windows and tables.
     Against the oracle; the fused call equals partials + merge on a
     workspace full of garbage."""
     import torch
 
-    wmode = "kv_map" if mode == "degenerate" else mode
+    wmode = "kv_map" if mode in ("degenerate", "kv_map8") else mode
     w = wgen.make_custom(seed=77, n_seqs=64, n_q_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
-                         fmts=fmts, ctx=(1500, 6000), mode=wmode, n_runs=3, max_blocks=2048)
+                         fmts=fmts, ctx=(1500, 6000), mode=wmode, n_runs=8 if mode == "kv_map8" else 3,
+                         max_blocks=2048)
     if mode == "degenerate":
         w.seq_lens[0] = 0                 # empty sequence
         w.kv_map[1] = 0                   # no runs

@@ -31,23 +31,33 @@ def _capture(fn):
     return g
 
 
-def test_decode_graph_replays_equal_eager():
+@pytest.mark.parametrize("kind", ["direct", "planned"])
+def test_decode_graph_replays_equal_eager(kind):
+    """direct: a small call (one workgroup per possible slot); planned: 64
+    sequences x 32 possible 1024-position slots x 8 kv heads, so the call
+    runs the plan kernel (work list, cut slots) inside the graph."""
     import torch
 
-    w = wgen.make_custom(seed=17, n_seqs=9, n_q_heads=16, n_kv_heads=4, head_dim=128, block_size=16,
-                         ctx=(1, 900), mode="kv_map", n_runs=4, hole_frac=0.1)
+    if kind == "direct":
+        w = wgen.make_custom(seed=17, n_seqs=9, n_q_heads=16, n_kv_heads=4, head_dim=128, block_size=16,
+                             ctx=(1, 900), mode="kv_map", n_runs=4, hole_frac=0.1)
+        split = 0
+    else:
+        w = wgen.make_custom(seed=18, n_seqs=64, n_q_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                             ctx=(1500, 6000), mode="kv_map", n_runs=4, hole_frac=0.1, max_blocks=2048)
+        split = 1024
     d = Dev(w)
-    want_o, want_l = d.decode()
-    shape = pkv.make_shape(d.q, d.k, d.v, d.table, w.n_seqs, w.scale)
+    want_o, want_l = d.decode(split_tokens=split)
+    shape = pkv.make_shape(d.q, d.k, d.v, d.table, w.n_seqs, w.scale, 0, split)
     ws = torch.empty(pkv.decode_workspace_bytes(shape, "kv_map", w.kv_map.shape[1]), dtype=torch.uint8,
                      device="cuda")
     out = torch.empty_like(want_o)
     lse = torch.empty_like(want_l)
-    g = _capture(lambda: d.decode(out=out, lse=lse, workspace=ws))
+    g = _capture(lambda: d.decode(out=out, lse=lse, workspace=ws, split_tokens=split))
     for i in range(4):
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
-        other_o, _ = d.decode()  # eager work between replays, on its own buffers
+        other_o, _ = d.decode(split_tokens=split)  # eager work between replays, on its own buffers
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, want_o) and torch.equal(lse, want_l), f"replay {i}"
