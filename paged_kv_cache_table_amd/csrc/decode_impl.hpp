@@ -285,6 +285,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
     lo = __builtin_amdgcn_readfirstlane((int)it.y);
     hi = __builtin_amdgcn_readfirstlane((int)it.z);
     prow = (uint32_t)__builtin_amdgcn_readfirstlane((int)it.w);
+    // An entry that is not an item of this call (the list is only valid
+    // right after the plan pass of the same call) is skipped rather than
+    // followed out of bounds: sequence, range within the table and inside
+    // one aligned split, and row are all checked.
+    if ((uint32_t)s >= (uint32_t)a.n_seqs || lo < 0 || hi <= lo || (int64_t)hi > (int64_t)a.max_blocks * BS ||
+        hi - lo > a.split || (hi - 1) / BS - lo / BS >= 64 || prow >= (int64_t)a.n_seqs * a.rows_per_seq)
+      return;
   } else {
     kvh = blockIdx.x;
     const int slot = blockIdx.y;
