@@ -229,12 +229,13 @@ size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t r
  * [seg] (device; seg_bytes_k / seg_bytes_v bytes per token per kv head, a
  * multiple of 4); a row is one slot of every kv head, so a move carries all
  * kv heads of its tokens.  The host plans the moves (order_moves, then the
- * final source of every changed row), uploads the plan into the workspace
- * and waits for that upload (and so for the work queued before it on
- * `stream`), so `moves` may be freed on return; the copies run
- * asynchronously on `stream`.  The upload goes through a pinned host buffer
- * that the library allocates on first use, grows to the largest plan seen
- * and keeps until the process ends; concurrent calls take turns on it.
+ * final source of every changed row) and writes the plan into one of two
+ * pinned host buffers that the library keeps per device (allocated on first
+ * use, grown to the largest plan seen, kept until the process ends;
+ * concurrent calls take turns on them), from which it is copied into the
+ * workspace on `stream`.  `moves` may be freed on return; the upload and the
+ * copies run asynchronously on `stream`.  A call waits only for the previous
+ * upload out of the same pinned buffer, never for the rest of the stream.
  * Every move must lie inside [0, n_pool_blocks * block_size) or the call is
  * refused untouched. */
 pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, int32_t block_size,
