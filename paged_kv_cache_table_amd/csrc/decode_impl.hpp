@@ -247,8 +247,26 @@ struct QElem<kComboQ8F> { using T = float; };
 
 // --------------------------------------------------------------------------
 
+// Waves per SIMD and register budget of an instance: three waves (a ring
+// of at least two passes next to q, the running outputs and ~24
+// temporaries, in ~152 VGPRs) where they fit, else no bound on the waves
+// and a ring sized for ~232 VGPRs (two waves per SIMD; the eight-head
+// groups need more and run one).  With the work list keeping every wave slot busy, the third wave
+// hides the start of each unit better than a deeper ring does (7B-class
+// split pass 734-736 against 739-744 us; long context and SmolLM2-like
+// batches also a little faster).
+template <int HD, int G, int COMBO>
+struct SplitRegs {
+  using KP = typename Paths<HD, G, COMBO>::K;
+  using VP = typename Paths<HD, G, COMBO>::V;
+  static constexpr int kBase = KP::kQRegs + 16 * G + 24;
+  static constexpr int kUnitRegs = KP::KW + VP::VW;
+  static constexpr int kWaves = kBase + 2 * kUnitRegs <= 152 ? 3 : 1;  // launch bound
+  static constexpr int kBudget = (kWaves == 3 ? 152 : 232) - kBase;
+};
+
 template <int HD, int BS, int G, int COMBO>
-__global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_split_kernel(AttnArgs a) {
   using KP = typename Paths<HD, G, COMBO>::K;
   using VP = typename Paths<HD, G, COMBO>::V;
   using QT = typename QElem<COMBO>::T;
@@ -257,10 +275,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnArgs a) {
   static_assert(BS % TPP == 0, "block size must be a multiple of tokens per pass");
   constexpr int NU = BS / TPP;  // passes per block; a pass is the pipelined unit
   constexpr int KW = KP::KW, VW = VP::VW;
-  // Register ring of one-pass units: as many as fit next to q, the running
-  // outputs and the temporaries in 256 VGPRs (2 waves per SIMD); the loads
-  // run RING-1 units ahead of compute.
-  constexpr int kBudget = 232 - KP::kQRegs - 16 * G - 24;
+  // Register ring of one-pass units: as many as fit the instance's budget
+  // next to q, the running outputs and the temporaries; the loads run
+  // RING-1 units ahead of compute.
+  constexpr int kBudget = SplitRegs<HD, G, COMBO>::kBudget;
   constexpr int kRingFit = kBudget / (KW + VW);
   constexpr int RING = kRingFit < 2 ? 2 : (kRingFit > 8 ? 8 : kRingFit);
   constexpr float kEmpty = -1e30f;  // running max before any visible token
