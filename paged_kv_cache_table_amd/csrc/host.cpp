@@ -177,13 +177,13 @@ pkv_status plan_decode(const pkv_shape* sh, int mode, int n_runs, const void* wi
                 (long long)(nspl * P->runs), sh->max_blocks_per_seq, sh->block_size, split, P->runs);
   P->split = split;
   P->nspl = (int)nspl;
-  // Calls that can have more than four rounds of units for the device's
-  // wave slots (taken as 2048) run the plan pass: the items without gaps,
-  // ending on short units, for which each sequence cuts its last few full
-  // slots into pieces of >= 256 positions, about two rounds' worth of
-  // pieces over the whole batch (at most kMaxCutPerSeq per sequence).
-  // Smaller calls launch one workgroup per possible slot: there the plan
-  // pass would cost more than it saves.
+  // Calls that can have more than kPlanMinUnits units run the plan pass:
+  // the items without gaps, ending on short units, for which each sequence
+  // cuts its last few full slots into pieces of >= 256 positions, about
+  // kCutWaves units of pieces over the whole batch (at most kMaxCutPerSeq
+  // slots per sequence).  Smaller calls launch one workgroup per possible
+  // slot: there the plan pass costs more than it saves (measured on a
+  // long-context batch of exactly 8192 possible units, all non-empty).
   constexpr int64_t kPlanMinUnits = 4 * 2048, kCutWaves = 4096, kMaxCutPerSeq = 2;
   const int64_t slots_per_seq = nspl * P->runs;
   P->planned = (int64_t)sh->n_seqs * slots_per_seq * sh->n_kv_heads > kPlanMinUnits;
