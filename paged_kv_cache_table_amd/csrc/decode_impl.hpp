@@ -495,20 +495,27 @@ hipError_t launch_split_instance(const AttnArgs& a, int64_t max_units, hipStream
 
 // Merge the partials of each (sequence, q head) by log-sum-exp:
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, lse = (M + log2 L) ln 2.
-// One workgroup per (256 consecutive (q head, dim) outputs, sequence): each
-// thread owns one output and merges the partials in a fixed order (slot
-// order; a cut slot's own row, then its pieces) with a running max,
-// rescaling when it grows, so a single pass suffices and results are
-// deterministic; the loads of eight rows are issued before their
-// arithmetic.  Which slots exist, and which are cut, follows from the
-// sequence's own length and window, exactly as the plan pass decides.
-template <int HD>
+// Four waves per workgroup, one lane per (q head, dim) output, so each load
+// is 256 contiguous bytes.  merge_split = 1: each wave merges all rows of
+// its own 64 outputs (256 outputs per workgroup).  merge_split = 4 (grids
+// too small to fill the device that way): the four waves share 64 outputs,
+// wave w merging rows w, w + 4, ..., and wave 0 combines the four results
+// in wave order through LDS.  Within a wave the rows go in order with a
+// running max, the loads of eight rows issued before their arithmetic.
+// Fixed order for a given shape, so results are deterministic.
+// A run's non-empty slots and their pieces hold one contiguous range of
+// rows, found from the run's bounds exactly as the plan pass places them.
+template <int HD, int NW>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
-  constexpr int kUnroll = 8;
+  constexpr int kUnroll = 8, kWaves = 4;
+  __shared__ float part[3][kWaves - 1][64];
   const int s = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;  // q head * HD + dim
-  if (idx >= a.n_q_heads * HD) return;
-  const int h = idx / HD, d = idx - h * HD;
+  constexpr int nw = NW;  // waves per output group (merge_split): 1 or 4
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = wv / nw, phase = wv - grp * nw;
+  const int idx = (blockIdx.x * (kWaves / nw) + grp) * 64 + lane;  // q head * HD + dim
+  const bool live = idx < a.n_q_heads * HD;
+  const int h = live ? idx / HD : 0, d = live ? idx - h * HD : 0;
   const int32_t lim = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
   int32_t rl, rh;
   int nfull = 0;
@@ -518,17 +525,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   }
   const int first_cut = nfull - (nfull < a.fine_per_seq ? nfull : a.fine_per_seq);
   float m = -INFINITY, l = 0.f, acc = 0.f;
-  auto add = [&](float2 ml, float o) {
-    if (ml.x == -INFINITY) return;  // a partial that saw nothing carries no weight
-    const float mn = fmaxf(m, ml.x);
-    const float ca = fast_exp2(m - mn), cb = fast_exp2(ml.x - mn);  // m = -inf -> ca = 0
-    acc = acc * ca + cb * o;
-    l = l * ca + cb * ml.y;
+  // merge (m2, l2, o2) into the running (m, l, acc); a partial that saw
+  // nothing (m2 = -inf) carries no weight, and an empty running value (m =
+  // -inf, l = acc = 0) is scaled by 2^-inf = 0
+  auto add = [&](float m2, float l2, float o2) {
+    if (m2 == -INFINITY) return;
+    const float mn = fmaxf(m, m2);
+    const float ca = fast_exp2(m - mn), cb = fast_exp2(m2 - mn);
+    acc = acc * ca + o2 * cb;
+    l = l * ca + l2 * cb;
     m = mn;
   };
-  // A run's non-empty slots k0..k1, each followed by its pieces when cut,
-  // hold one contiguous range of rows: row(slot) = slot + (cut slots
-  // before it) * (nsub - 1).
+  // row(slot) = slot + (cut slots before it) * (nsub - 1)
   int full_before = 0;
   for (int r = 0; r < a.n_runs; ++r) {
     run_range(a, s, r, lim, rl, rh);
@@ -540,23 +548,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     full_before += nf;
     const int64_t row_a = (int64_t)s * a.rows_per_seq + (int64_t)r * a.nspl + k0 + (int64_t)cut0 * (a.nsub - 1);
     const int n_rows = k1 - k0 + 1 + (cut1 - cut0) * (a.nsub - 1);
-    for (int i0 = 0; i0 < n_rows; i0 += kUnroll) {
+    for (int i0 = phase; live && i0 < n_rows; i0 += nw * kUnroll) {
       float2 ml[kUnroll];
       float o[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         ml[u] = make_float2(-INFINITY, 0.f);
         o[u] = 0.f;
-        if (i0 + u < n_rows) {
-          const int64_t row = (row_a + i0 + u) * a.n_q_heads + h;
+        const int i = i0 + nw * u;
+        if (i < n_rows) {
+          const int64_t row = (row_a + i) * a.n_q_heads + h;
           ml[u] = *(const float2*)(a.part_ml + row * 2);
           o[u] = a.part_o[row * HD + d];
         }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) add(ml[u], o[u]);
+      for (int u = 0; u < kUnroll; ++u) add(ml[u].x, ml[u].y, o[u]);
     }
   }
+  if constexpr (nw > 1) {
+    if (phase > 0) {
+      part[0][phase - 1][lane] = m;
+      part[1][phase - 1][lane] = l;
+      part[2][phase - 1][lane] = acc;
+    }
+    __syncthreads();
+    if (phase > 0) return;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves - 1; ++w2) add(part[0][w2][lane], part[1][w2][lane], part[2][w2][lane]);
+  }
+  if (!live) return;
   const int64_t oi = ((int64_t)s * a.n_q_heads + h) * HD + d;
   if (m == -INFINITY) {
     a.out[oi] = 0.f;

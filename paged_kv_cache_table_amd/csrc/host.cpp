@@ -289,6 +289,10 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
   a.fine_tokens = P.fine;
   a.fine_per_seq = P.fine_per_seq;
   a.rows_per_seq = P.rows_per_seq;
+  // The merge splits each output's rows over four waves when one wave per
+  // 64 outputs would give fewer than 512 workgroups (too few to fill the
+  // device); else each wave keeps its own outputs.  Depends on the shape only.
+  a.merge_split = (int64_t)sh->n_seqs * ((sh->n_q_heads * sh->head_dim + 255) / 256) < 512 ? 4 : 1;
   a.seqinfo = (uint4*)((char*)ws + P.off_seq);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;

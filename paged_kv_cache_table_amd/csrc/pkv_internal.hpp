@@ -45,6 +45,7 @@ struct AttnArgs {
   uint4* seqinfo;
   int32_t nsub, fine_tokens, fine_per_seq;
   int64_t rows_per_seq;
+  int32_t merge_split;  // decode merge: waves sharing one group of outputs (1 or 4)
   int32_t n_q_total, max_q;
   int32_t nch;           // prefill: chunks each workgroup's window is split into
   // Pool layout [n_blocks][n_kv_heads][block_size][seg]: seg = bytes of one
@@ -210,7 +211,7 @@ hipError_t launch_decode_plan(const AttnArgs& a, hipStream_t st);
 // Decode split pass: grid max_units (the host's bound on units) x 64 threads.
 hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int g,
                                int64_t max_units, hipStream_t st, bool* found);
-// Decode merge pass: grid (ceil(n_q_heads * head_dim / 256), n_seqs), 256 threads.
+// Decode merge pass: grid (ceil(n_q_heads * head_dim / (256 / merge_split)), n_seqs), 256 threads.
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
 // Prefill: workspace bytes a call needs (a multiple of 256, the last 256
 // bytes hold the checked-mode error word; 0 if none) and whether a kernel
