@@ -27,9 +27,9 @@
 // (global_load_lds: no registers in between), two tiles ahead of the
 // compute, into a ring of three tile slots; it then waits for its own copies
 // only (vmcnt) and prepares its rows (V rows of positions that are not
-// visible zeroed; a q8_0 value x = scale * code, exact in f32, split into
-// hi = f16(x) and lo = f16(x - hi), which represent x exactly for every f16
-// scale and int8 code), so one barrier per tile suffices.  f16 rows are
+// visible zeroed; q8_0 K rows become their int8 codes as f16, which is exact,
+// and the block scales are kept apart as f32), so one barrier per tile
+// suffices.  f16 rows are
 // stored row-major with their 16-byte chunks XOR-swizzled by the row index,
 // which keeps both the score-operand reads and the transposing V reads free
 // of bank conflicts.
@@ -40,8 +40,11 @@
 // operand of O^T = V^T P^T.  Its A operand (a head_dim column of V over those
 // positions) comes from ds_read_b64_tr_b16: within each 16-lane group, lane i
 // receives element i % 4 of the 4 halves that lane 4 e + i / 4 addressed, as
-// element e.  For q8_0 K the scores are K_hi Q^T + K_lo Q^T: the products are
-// exact in f32, so the dequantised value is never rounded.  The row sums of
+// element e.  For q8_0 K each 32-wide MFMA k-step covers exactly one q8_0
+// block of every position, so it multiplies the codes (exact in f16) by q
+// and the block scale of each position is applied to that partial in f32:
+// no product of scale and code is ever formed in f16, whatever the scale
+// (any f16 value, 65504 included).  The row sums of
 // the rounded probabilities come from one more MFMA per PV step whose A
 // operand is all ones (the same rounded values as the numerator).  Positions
 // outside the run, in a hole or past a row's causal limit score -inf; a tile
@@ -104,9 +107,11 @@ template <int HD, bool KQ8>
 struct __attribute__((aligned(16))) PrefillSmem {
   using Gm = PGeom<HD>;
   unsigned char v[kRing][Gm::TILEB];                                  // V tiles
-  // K tiles: f16 as copied, or q8_0 widened into the pair (hi, lo) of f16
-  // tiles with hi + lo == scale * code exactly
-  unsigned char k[KQ8 ? 2 : kRing][KQ8 ? 2 : 1][Gm::TILEB];
+  // K tiles: f16 as copied, or the int8 codes of q8_0 rows as f16 values
+  unsigned char k[KQ8 ? 2 : kRing][Gm::TILEB];
+  // q8_0: the block scales as f32, [ks][position] (4 consecutive positions
+  // of one k-step are one 16-byte read)
+  float ksc[KQ8 ? 2 : 1][KQ8 ? Gm::KS : 1][KQ8 ? Gm::T : 4];
   unsigned char raw[KQ8 ? kRing : 1][KQ8 ? kPWaves * Gm::RAWW : 16];  // q8_0 tiles as stored
   TileRec tiles[kMaxTiles];                                           // this workgroup's chunk
   int32_t lim_max;                                                    // largest causal limit of the rows
@@ -409,7 +414,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     for (int i = 0; i < Gm::NV; ++i) {
       copy16_to_lds(vb, voff[i], lv + i * 1024);
       if constexpr (!KQ8) {
-        const uint32_t lk = (uint32_t)uni((int32_t)lds_addr(&sm.k[sl][0][pw0 * Gm::ROWB]));
+        const uint32_t lk = (uint32_t)uni((int32_t)lds_addr(&sm.k[sl][pw0 * Gm::ROWB]));
         copy16_to_lds(kb, voff[i], lk + i * 1024);
       }
     }
@@ -424,8 +429,9 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     }
   };
 
-  // after this wave's copies of a tile landed: widen its q8_0 rows into
-  // K slot kb and zero the V rows of its positions that are not visible
+  // after this wave's copies of a tile landed: turn its q8_0 rows into f16
+  // codes in K slot kb and f32 scales, and zero the V rows of its positions
+  // that are not visible (their codes and scales become 0 as well)
   auto prepare = [&](int sl, int kb, const TileD& d) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -447,8 +453,9 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
           const int bq = rem >> 1, h = rem & 1;
           const int r = pw0 + p;
           const bool ok = (d.vm >> r) & 1ull;
-          // bytes [lb, lb + 18) of the segment: f16 scale (used when h == 0)
-          // then 16 codes; lb is even, read as five aligned dwords
+          // bytes [lb, lb + 18) of the segment: the f16 scale (h == 0) or the
+          // last two codes of the first half (h == 1), then 16 codes; lb is
+          // even, read as five aligned dwords
           const int lb = 34 * bq + 16 * h;
           const uint32_t* src = (const uint32_t*)&sm.raw[sl][w * Gm::RAWW + p * Gm::SEG8 + (lb & ~3)];
           uint32_t qw[5];
@@ -461,40 +468,22 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
             cw[i] = sh ? qw[i + 1] : __builtin_amdgcn_alignbyte(qw[i + 1], qw[i], 2);
             cw[i] = ok ? cw[i] : 0u;
           }
-          // the block scale sits in the bytes of the h == 0 unit, which is
-          // the even lane of each lane pair: take it from there
-          const uint32_t sw = ok ? (sh ? (qw[0] >> 16) : (qw[0] & 0xFFFFu)) : 0u;
-          const uint32_t sw0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sw, 0xA0, 0xF, 0xF, false);
-          const _Float16 s16 = __builtin_bit_cast(_Float16, (unsigned short)sw0);
-          const half2_t s2 = {s16, s16};
-          // x = scale * code exactly as hi + lo, two values per instruction:
-          // hi = RN16(code * scale) (packed multiply); code * scale has at
-          // most 18 significant bits, all multiples of the scale's ulp
-          // (>= 2^-24), so lo = code * scale - hi fits an f16 and the packed
-          // fused multiply-add computes it exactly
-          half8_t hi8[2], lo8[2];
+          if (h == 0) {
+            const uint32_t sw = ok ? (sh ? (qw[0] >> 16) : (qw[0] & 0xFFFFu)) : 0u;
+            sm.ksc[kb][bq][r] = (float)__builtin_bit_cast(_Float16, (unsigned short)sw);
+          }
+          half8_t c8[2];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             half2_t c01, c23;
             codes_to_f16(cw[i], c01, c23);
-            const half2_t h01 = c01 * s2, h23 = c23 * s2;
-            const half2_t l01 = __builtin_elementwise_fma(c01, s2, -h01);
-            const half2_t l23 = __builtin_elementwise_fma(c23, s2, -h23);
-            hi8[i >> 1][4 * (i & 1) + 0] = h01[0];
-            hi8[i >> 1][4 * (i & 1) + 1] = h01[1];
-            hi8[i >> 1][4 * (i & 1) + 2] = h23[0];
-            hi8[i >> 1][4 * (i & 1) + 3] = h23[1];
-            lo8[i >> 1][4 * (i & 1) + 0] = l01[0];
-            lo8[i >> 1][4 * (i & 1) + 1] = l01[1];
-            lo8[i >> 1][4 * (i & 1) + 2] = l23[0];
-            lo8[i >> 1][4 * (i & 1) + 3] = l23[1];
+            c8[i >> 1][4 * (i & 1) + 0] = c01[0];
+            c8[i >> 1][4 * (i & 1) + 1] = c01[1];
+            c8[i >> 1][4 * (i & 1) + 2] = c23[0];
+            c8[i >> 1][4 * (i & 1) + 3] = c23[1];
           }
 #pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) {
-            const int off = swz<HD>(r, 4 * bq + 2 * h + e2);
-            *(half8_t*)&sm.k[kb][0][off] = hi8[e2];
-            *(half8_t*)&sm.k[kb][1][off] = lo8[e2];
-          }
+          for (int e2 = 0; e2 < 2; ++e2) *(half8_t*)&sm.k[kb][swz<HD>(r, 4 * bq + 2 * h + e2)] = c8[e2];
         }
       }
     }
@@ -502,8 +491,10 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
 
   // S^T = K Q^T for the 32-position half kh of a tile: for 16-position tile
   // st the lane holds positions 16 st + 4 g + i of the half, for row n16, as
-  // sc[rt][4 st + i]
-  auto scores = [&](const unsigned char* kt, int kh, float (&sc)[RT][8]) {
+  // sc[rt][4 st + i].  q8_0: the k-step ks is q8_0 block ks of each position;
+  // its MFMA partial (codes times q, products exact in f32) is scaled by the
+  // four positions' block scales (ksl: [ks][position] of this tile).
+  auto scores = [&](const unsigned char* kt, const float* ksl, int kh, float (&sc)[RT][8]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int krow = 32 * kh + 16 * st + n16;
@@ -514,12 +505,17 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       for (int ks = 0; ks < KS; ++ks) {
         const int off = swz<HD>(krow, 4 * ks + g);
         const half8_t af = *(const half8_t*)&kt[off];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma16x16x32(af, qf[rt][ks], acc[rt]);
         if constexpr (KQ8) {
-          const half8_t al = *(const half8_t*)&kt[Gm::TILEB + off];  // the lo tile follows the hi tile
+          const float4_t s4 = *(const float4_t*)&ksl[ks * T + 32 * kh + 16 * st + 4 * g];
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma16x16x32(al, qf[rt][ks], acc[rt]);
+          for (int rt = 0; rt < RT; ++rt) {
+            const float4_t pk = mfma16x16x32(af, qf[rt][ks], float4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rt][i] = fmaf(pk[i], s4[i], acc[rt][i]);
+          }
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma16x16x32(af, qf[rt][ks], acc[rt]);
         }
       }
 #pragma unroll
@@ -535,12 +531,13 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   // max of the current half and interleaved with its exponentials (vector
   // ALU), so the two overlap.
   auto compute = [&](int sl, int kb, const TileD& d) {
-    const unsigned char* kt = KQ8 ? sm.k[kb][0] : sm.k[sl][0];
+    const unsigned char* kt = KQ8 ? sm.k[kb] : sm.k[sl];
+    const float* ksl = &sm.ksc[KQ8 ? kb : 0][0][0];
     const unsigned char* vt = sm.v[sl];
     const half8_t ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
                           (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
     float sc[RT][8], sn[RT][8];
-    scores(kt, 0, sn);
+    scores(kt, ksl, 0, sn);
 #pragma unroll
     for (int kh = 0; kh < NKH; ++kh) {
 #pragma unroll
@@ -587,7 +584,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       }
       // the next half's scores (matrix cores) next to this half's
       // exponentials (vector ALU): one basic block, so they interleave
-      if (kh + 1 < NKH) scores(kt, kh + 1, sn);
+      if (kh + 1 < NKH) scores(kt, ksl, kh + 1, sn);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -624,8 +621,8 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       // each pair of score MFMAs, and the V reads of the PV step again run
       // four ahead.  Masks: 0x100 LDS read, 0x008 MFMA, 0x002 vector ALU.
       if (kh + 1 < NKH) {
-        constexpr int kSM = 2 * KS * RT * (KQ8 ? 2 : 1);  // score MFMAs of a half
-        constexpr int kSR = 2 * KS * (KQ8 ? 2 : 1);       // their K fragment reads
+        constexpr int kSM = 2 * KS * RT;             // score MFMAs of a half
+        constexpr int kSR = 2 * KS * (KQ8 ? 2 : 1);  // their K fragment (and q8_0 scale) reads
         constexpr int kPM = (DT + 1) * RT;                // PV and row-sum MFMAs
         constexpr int kPR = 2 * DT;                       // V reads
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
