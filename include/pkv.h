@@ -174,6 +174,29 @@ pkv_status pkv_paged_attn_decode_merge(const pkv_shape* shape, const int32_t* se
                                        size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and refusals as
+ * pkv_paged_attn_decode; the workspace is a built-in device array of
+ * PKV_NOALLOC_SCRATCH_BYTES bytes (each GPU holds its own copy from the
+ * library's first use until the process ends; its address is looked up on
+ * the first call on each device).  The call allocates nothing.  A call whose
+ * pkv_decode_workspace_bytes exceeds the array is refused with
+ * PKV_E_WORKSPACE before anything is launched (the 7B-class batch of 64
+ * sequences of up to 32,768 tokens, 32/8 heads, head_dim 128, needs ~41 MB).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (two streams, or two threads) race on it and give undefined results;
+ * calls ordered on one stream are safe.  The array needs no clearing between
+ * calls (the decode passes write everything they read).
+ * ------------------------------------------------------------------------- */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+pkv_status pkv_paged_attn_decode_noalloc(const pkv_shape* shape, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* block_table,
+                                         const int32_t* seq_lens, int32_t mode, int32_t n_runs,
+                                         const int32_t* window, float* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Windowed prefill: a chunk of queries per sequence against its window,
  * causal inside the window ("KV Cache Design", section 1: the fast windowed
  * prefill families for more than one query).  QK^T and PV run on the matrix

@@ -35,6 +35,7 @@ EXPORTS = (
     "pkv_row_bytes",
     "pkv_decode_workspace_bytes",
     "pkv_decode_split_tokens",
+    "pkv_paged_attn_decode_noalloc",
     "pkv_paged_attn_decode",
     "pkv_paged_attn_decode_partials",
     "pkv_paged_attn_decode_merge",
@@ -110,6 +111,7 @@ def lib() -> ctypes.CDLL:
         "pkv_paged_attn_decode": (I32, [SH, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
         "pkv_paged_attn_decode_partials": (I32, [SH, P, P, P, P, P, I32, I32, P, P, SZ, P]),
         "pkv_paged_attn_decode_merge": (I32, [SH, P, I32, I32, P, P, P, P, SZ, P]),
+        "pkv_paged_attn_decode_noalloc": (I32, [SH, P, P, P, P, P, I32, I32, P, P, P, P]),
         "pkv_prefill_workspace_bytes": (SZ, [SH, I32, I32, I32, I32]),
         "pkv_paged_attn_prefill_window": (I32, [SH, I32, I32, P, P, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
         "pkv_order_moves": (I32, [P, I32, P, P]),
@@ -329,6 +331,31 @@ def paged_attn_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, mo
                                              _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), st))
     else:
         raise ValueError(part)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attn_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, scale: float, out, lse,
+                              mode: str = "causal", window=None, flags: int = 0, split_tokens: int = 0):
+    """pkv_paged_attn_decode_noalloc: decode with the library's built-in
+    device scratch instead of a workspace (the call allocates nothing, so
+    out and lse must be given).  Arguments as for paged_attn_decode."""
+    torch = _torch()
+    _on_one_gpu(q, k_pool, v_pool, block_table, seq_lens, window, out, lse)
+    S = q.shape[0]
+    shape = make_shape(q, k_pool, v_pool, block_table, S, scale, flags, split_tokens)
+    _i32(seq_lens, "seq_lens")
+    m, n_runs, win = _window_args(mode, window)
+    i32, f32 = torch.int32, torch.float32
+    _sized(seq_lens, "seq_lens", S, i32)
+    _sized(win, "window", S * n_runs * 2, i32)
+    _sized(out, "out", S * shape.n_q_heads * shape.head_dim, f32)
+    _sized(lse, "lse", S * shape.n_q_heads, f32)
+    _check(lib().pkv_paged_attn_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                               _ptr(block_table), _ptr(seq_lens), m, n_runs, _ptr(win),
+                                               _ptr(out), _ptr(lse), _stream(q)))
     return out, lse
 
 
