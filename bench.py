@@ -5,17 +5,21 @@
 Default workload: decode on the 7B-class batch (64 sequences in 16 groups of
 4 copy-on-write forks sharing a 2048-token prefix, 32 q / 8 kv heads,
 head_dim 128, block 16, f16 K/V, 4096..32768 tokens each).  A step is one
-decode call (split pass + log-sum-exp merge) over the batch, with all inputs
-resident in HBM.  Prints one JSON line:
+pkv_paged_attn_decode call (plan, split and log-sum-exp merge kernels) over
+the batch, with all inputs resident in HBM.  Prints one JSON line:
 
 * value: effective KV bandwidth = logical K/V bytes the queries attend to
   (B_log: every visible token x kv head, K and V rows) / step time;
-* roofline: the split kernel's unique algorithmic bytes (B_uniq: each
-  physical K/V row once, plus q, table entries and partials) / its average
-  duration measured with HIP events on the stream it runs on, against the
-  8 TB/s HBM peak;
+* hbm_frac_step: B_uniq / step time / 8 TB/s, with B_uniq the call's
+  distinct bytes (each physical K/V row once, q, table entries, seq_lens,
+  out and lse, and the split partials written and read back);
+* pct_of_device_copy: the same rate against a plain device copy measured in
+  the same run;
+* roofline: the split kernel's algorithmic bytes / the average duration of
+  the call's partials half (plan + split kernels) from HIP events on the
+  stream it runs on, against the 8 TB/s HBM peak;
 * cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
-  workload on this host.
+  workload on this host, with the host's core counts and CPU model.
 
 Other workloads (for the record; the default is the headline): decode1,
 decode2, decode5, prefill4, copy5b, store4, cow3, defrag3, int4; and calib, a plain device copy of known
@@ -91,6 +95,32 @@ def decode_bytes(w):
     return b_log, b_uniq, vis
 
 
+def host_cpu_info():
+    """Host CPU facts for the baseline: logical CPUs, CPUs this process may
+    use, physical cores and the model name (from lscpu)."""
+    info = {"host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        import psutil
+
+        info["physical_cores"] = psutil.cpu_count(logical=False)
+    except Exception:  # pragma: no cover
+        info["physical_cores"] = None
+    model = None
+    try:
+        import subprocess
+
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+            if line.startswith("Core(s) per socket:") and info["physical_cores"] is None:
+                info["cores_per_socket"] = int(line.split(":", 1)[1])
+    except Exception:  # pragma: no cover
+        pass
+    info["cpu_model"] = model
+    return info
+
+
 def cpu_baseline_decode(w, d, budget_s=12.0):
     """Time the oracle on whole sequences of the workload until budget_s."""
     import oracle
@@ -118,17 +148,18 @@ def cpu_baseline_decode(w, d, budget_s=12.0):
         seqs.append(s)
         if t_total >= budget_s:
             break
-    return {
+    res = {
         "value": round(done_bytes / t_total / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"float64 numpy oracle on {len(seqs)} of {w.n_seqs} sequences "
-                  f"({sum(vis[s] for s in seqs)} visible tokens, {t_total:.1f} s; excludes host copies)",
-        "host_cpus": os.cpu_count(),
-        "affinity_cpus": len(os.sched_getaffinity(0)),
+                  f"({sum(vis[s] for s in seqs)} visible tokens, {t_total:.1f} s; excludes host copies); "
+                  f"cores = BLAS threads the oracle's products ran on",
         "queries_per_s": round(len(seqs) / t_total, 4),
     }
+    res.update(host_cpu_info())
+    return res
 
 
 def sources_hash(paths) -> str:
@@ -222,7 +253,37 @@ def run_calib(args):
             "ms_per_copy": round(ms, 4), "GBps_read_plus_write": round(2 * CALIB_BYTES / (ms * 1e-3) / 1e9, 1)}
 
 
+def decode_partial_rows(w, split, planned_units_min=4 * 2048):
+    """Partial rows a decode call writes (and its merge reads): one per
+    non-empty split slot of each sequence, plus the extra pieces of the slots
+    a planned call cuts (each sequence's last min(2, ceil(4096 / (pieces x
+    kv heads x seqs))) full slots, cut into pieces of >= 256 positions).
+    Causal windows; this mirrors the split rule of the library's decode."""
+    bs, S, hkv = w.block_size, w.n_seqs, w.n_kv_heads
+    nspl = -(-w.max_blocks_per_seq * bs // split)
+    planned = S * nspl * hkv > planned_units_min
+    nsub = max(1, min(4, split // 256))
+    fine = -(-(-(-split // nsub)) // bs) * bs
+    while nsub > 1 and (nsub - 1) * fine >= split:
+        nsub -= 1
+    fine_per_seq = 0
+    if planned and nsub > 1:
+        fine_per_seq = min(2, -(-4096 // (nsub * hkv * S)), nspl)
+    rows = 0
+    for L in w.seq_lens:
+        L = int(L)
+        rows += -(-L // split) + min(fine_per_seq, L // split) * (nsub - 1)
+    return rows
+
+
 def run_decode(cfg, args):
+    """Decode headline: one fused pkv_paged_attn_decode call (split + merge
+    kernels, and the plan kernel for batches of more than 256 sequences) per
+    step.  Three passes over the same inputs after the warm-up: one call at
+    a time between HIP events on the stream the library launches on
+    (event_ms); the two halves of the call (partials = plan + split kernels,
+    then merge) between events, for the dominant-kernel roofline; and last,
+    back to back by wall clock (ms_per_step, value)."""
     import torch
 
     import paged_kv_cache_table_amd as pkv
@@ -239,61 +300,81 @@ def run_decode(cfg, args):
     lse = torch.empty((w.n_seqs, w.n_q_heads), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def call(part="both"):
         pkv.paged_attn_decode(q, k, v, table, lens, w.scale, out=out, lse=lse, workspace=ws,
-                              split_tokens=args.split, part="partials")
-        if ev is not None:
-            ev[1].record(stream)
-        pkv.paged_attn_decode(q, k, v, table, lens, w.scale, out=out, lse=lse, workspace=ws,
-                              split_tokens=args.split, part="merge")
-        if ev is not None:
-            ev[2].record(stream)
+                              split_tokens=args.split, part=part)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # host-side byte counts first, so that the timed passes follow the
+    # warm-up directly (an idle GPU clocks down)
     b_log, b_uniq_kv, vis = decode_bytes(w)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
     # A batch whose K/V fit in the 256 MB Infinity Cache would be timed from
     # the cache: evict before every timed step and time each step with events
     # (the eviction itself stays outside); the warm figure is kept, labelled.
     cold = b_uniq_kv < (1 << 30)
     flush = ColdCache() if cold else None
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps" + (" (caches evicted before each)" if cold else ""))
-    warm_ms = None
-    if cold:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        for i in range(args.steps):
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # pass 1: one fused call per step between events
+    call_ms = []
+    for _ in range(args.steps):
+        if cold:
             flush()
-            step(evs[i])
-        torch.cuda.synchronize()
-    else:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(evs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    split_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    ms = float(np.mean(step_ms)) if cold else wall * 1e3 / args.steps
-    # algorithmic bytes of one split launch: unique K/V rows + q + table
-    # entries read + seq_lens + partials written
-    q_bytes = q.numel() * q.element_size()
-    table_bytes = sum((int(L) + w.block_size - 1) // w.block_size for L in w.seq_lens) * 4 * w.n_kv_heads
-    G = w.group
+        e = [ev(), ev()]
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+        if cold:
+            torch.cuda.synchronize()
+        call_ms.append(e)
+    torch.cuda.synchronize()
+    call_ms = [e[0].elapsed_time(e[1]) for e in call_ms]
+    # pass 2: the two halves of the call
+    halves = []
+    for _ in range(args.steps):
+        if cold:
+            flush()
+        e = [ev(), ev(), ev()]
+        e[0].record(stream)
+        call("partials")
+        e[1].record(stream)
+        call("merge")
+        e[2].record(stream)
+        if cold:
+            torch.cuda.synchronize()
+        halves.append(e)
+    torch.cuda.synchronize()
+    # pass 3: back to back, wall clock (no events in the stream), last, so
+    # that it runs at the clocks of a GPU that has been busy
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    part_ms = [e[0].elapsed_time(e[1]) for e in halves]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in halves]
+    ms = float(np.mean(call_ms)) if cold else wall_ms
+
+    # algorithmic bytes of the whole call (B_uniq): distinct K/V rows, q, the
+    # table entries and seq_lens read, out and lse written, and the split
+    # partials written by the split kernel and read by the merge
+    G, hd = w.group, w.head_dim
     split = pkv.decode_split_tokens(shape)
-    items = sum(-(-int(L) // split) for L in w.seq_lens) * w.n_kv_heads
-    part_bytes = items * G * (w.head_dim + 2) * 4
-    alg = b_uniq_kv + q_bytes + table_bytes + part_bytes
-    split_avg_ms = float(np.mean(split_ms))
-    achieved = alg / (split_avg_ms * 1e-3) / 1e9
+    rows = decode_partial_rows(w, split)
+    q_bytes = q.numel() * q.element_size()
+    table_bytes = sum((int(L) + w.block_size - 1) // w.block_size for L in w.seq_lens) * 4
+    lens_bytes = 4 * w.n_seqs
+    out_bytes = out.numel() * 4 + lse.numel() * 4
+    part_bytes = rows * w.n_q_heads * (hd + 2) * 4
+    b_uniq = b_uniq_kv + q_bytes + table_bytes + lens_bytes + out_bytes + 2 * part_bytes
+    # the split kernel's own bytes: K/V, q, table, seq_lens, partials written
+    alg_split = b_uniq_kv + q_bytes + table_bytes + lens_bytes + part_bytes
+    part_avg = float(np.mean(part_ms))
+    achieved = alg_split / (part_avg * 1e-3) / 1e9
+    copy = measure_copy_GBps()
+    step_gbs = b_uniq / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(b_log / (ms * 1e-3) / 1e9, 2),
@@ -314,36 +395,73 @@ def run_decode(cfg, args):
             "seqs": w.n_seqs,
             "visible_tokens": int(sum(vis)),
             "B_log_bytes": int(b_log),
-            "B_uniq_kv_bytes": int(b_uniq_kv),
+            "B_uniq_bytes": int(b_uniq),
+            "B_uniq_parts": {"kv": int(b_uniq_kv), "q": q_bytes, "table": table_bytes, "seq_lens": lens_bytes,
+                             "out_lse": out_bytes, "partials_written_and_read": 2 * part_bytes},
             "split_tokens": int(split),
+            "partial_rows": int(rows),
         },
-        "timing": ("HIP events per step, caches evicted before each step" if cold
-                   else "wall clock over back-to-back steps"),
+        "step": "one pkv_paged_attn_decode call (split + merge kernels; a plan kernel first above 256 sequences)",
+        "timing": ("HIP events per call, caches evicted before each call" if cold
+                   else "wall clock over back-to-back calls"),
         "queries_per_s": round(w.n_seqs / (ms * 1e-3), 1),
-        "hbm_frac_uniq_step": round(b_uniq_kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "event_ms": {"step_median": round(float(np.median(step_ms)), 5),
-                     "step_p10": round(float(np.percentile(step_ms, 10)), 5),
-                     "step_p90": round(float(np.percentile(step_ms, 90)), 5),
-                     "split_avg": round(split_avg_ms, 5),
-                     "merge_avg": round(float(np.mean(merge_ms)), 5)},
+        # the headline fraction: B_uniq of the whole call / step time / 8 TB/s
+        "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
+        "uniq_GBps_step": round(step_gbs, 1),
+        "hbm_frac_call_median": round(b_uniq / (float(np.median(call_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "pct_of_device_copy": round(100 * step_gbs / copy["GBps_read_plus_write"], 1),
+        "device_copy": copy,
+        "event_ms": {"call_median": round(float(np.median(call_ms)), 5),
+                     "call_mean": round(float(np.mean(call_ms)), 5),
+                     "call_p10": round(float(np.percentile(call_ms, 10)), 5),
+                     "call_p90": round(float(np.percentile(call_ms, 90)), 5),
+                     "wall_back_to_back": round(wall_ms, 5),
+                     "partials_mean": round(part_avg, 5),
+                     "merge_mean": round(float(np.mean(merge_ms)), 5)},
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_split_kernel",
-            # the events bracket the partials call: the one-workgroup plan
-            # kernel (when the call is planned) and the split kernel
-            "timed": "decode partials call (decode_plan_kernel + decode_split_kernel)",
+            # events bracket the partials half of the call: the one-workgroup
+            # plan kernel (when the call is planned) and the split kernel
+            "timed": "decode partials call (decode_plan_kernel + decode_split_kernel), HIP events",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": stored_traffic("decode3") if cfg == 3 and not args.split else None,
-            "algorithmic_bytes": int(alg),
+            "algorithmic_bytes": int(alg_split),
         },
     }
-    if warm_ms is not None:
+    if cold:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         res["warm_unflushed"] = {"ms_per_step": round(warm_ms, 5),
                                  "GBps_B_log": round(b_log / (warm_ms * 1e-3) / 1e9, 2)}
     return res, w, {"q": q, "k": k, "v": v}
+
+
+def measure_copy_GBps(nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of `nbytes` on the same GPU, timed with
+    HIP events: read + write bytes per second (the secondary reference for
+    the decode figure)."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"bytes": 2 * nbytes, "ms": round(ms, 4), "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def prefill_work(w, dev):

@@ -172,20 +172,13 @@ hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int
 }
 
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st) {
-  const int per_wg = 256 / a.merge_split;  // outputs per workgroup
-  const dim3 grid((unsigned)((a.n_q_heads * hd + per_wg - 1) / per_wg), a.n_seqs);
-#define PKV_MERGE(HD)                                                                              \
-  case HD:                                                                                         \
-    if (a.merge_split == 4) hipLaunchKernelGGL((decode_merge_kernel<HD, 4>), grid, dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((decode_merge_kernel<HD, 1>), grid, dim3(256), 0, st, a);              \
-    break;
+  const dim3 grid((unsigned)((a.n_q_heads * hd + 255) / 256), a.n_seqs);
   switch (hd) {
-    PKV_MERGE(64)
-    PKV_MERGE(128)
-    PKV_MERGE(256)
+    case 64: hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL(decode_merge_kernel<256>, grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
-#undef PKV_MERGE
   return hipGetLastError();
 }
 

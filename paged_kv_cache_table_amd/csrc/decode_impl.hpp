@@ -247,6 +247,169 @@ struct QElem<kComboQ8F> { using T = float; };
 
 // --------------------------------------------------------------------------
 
+// The work list without the plan pass: item `it` of the list the plan pass
+// would write (whole full slots, then partial slots, then the pieces of cut
+// slots, each group in sequence order; see decode_plan_kernel), derived by
+// one wave from the sequences' lengths and windows.  Lane l holds sequences
+// l * SPL .. l * SPL + SPL - 1; three wave scans give each lane's place in
+// each group; the lane whose range holds `it` names the sequence, and the
+// sequence's runs give the slot.  Wave-uniform results.  Returns false when
+// `it` is past the list's end.
+__device__ inline bool self_plan_item(const AttnArgs& a, uint32_t it, int& s_out, int32_t& lo_out,
+                                      int32_t& hi_out, int64_t& row_out) {
+  constexpr int SPL = kSelfPlanMaxSeqs / 64;
+  const int lane = threadIdx.x & 63;
+  const int32_t split = a.split;
+  const uint32_t fps = (uint32_t)a.fine_per_seq;
+  uint32_t cnt[3][SPL], fcut[SPL];
+  uint32_t tot[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int s = lane * SPL + i;
+    uint32_t nact = 0, nfull = 0;
+    if (s < a.n_seqs) {
+      const int32_t L = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
+      for (int r = 0; r < a.n_runs; ++r) {
+        int32_t rl, rh;
+        run_range(a, s, r, L, rl, rh);
+        nact += rh > rl ? (uint32_t)((rh - 1) / split - rl / split + 1) : 0u;
+        nfull += (uint32_t)full_slots(rl, rh, split);
+      }
+    }
+    const uint32_t ncut = nfull < fps ? nfull : fps;
+    fcut[i] = nfull - ncut;
+    cnt[0][i] = nfull - ncut;
+    cnt[1][i] = nact - nfull;
+    cnt[2][i] = ncut;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) tot[c] += cnt[c][i];
+  }
+  // exclusive prefix over lanes of each group's lane total
+  uint32_t excl[3], all[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    uint32_t inc = tot[c];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    excl[c] = inc - tot[c];
+    all[c] = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  }
+  const uint32_t nsub = (uint32_t)a.nsub;
+  int grp;
+  uint32_t t;
+  if (it < all[0]) {
+    grp = 0;
+    t = it;
+  } else if (it - all[0] < all[1]) {
+    grp = 1;
+    t = it - all[0];
+  } else if ((it - all[0] - all[1]) / nsub < all[2]) {
+    grp = 2;
+    t = (it - all[0] - all[1]) / nsub;
+  } else {
+    return false;
+  }
+  // the lane whose sequences hold rank t of the group, then the sequence
+  uint32_t ex_g = grp == 0 ? excl[0] : (grp == 1 ? excl[1] : excl[2]);
+  uint32_t tot_g = grp == 0 ? tot[0] : (grp == 1 ? tot[1] : tot[2]);
+  const uint64_t above = __ballot(ex_g + tot_g > t);
+  const int ln = (int)__builtin_ctzll(above);
+  uint32_t rank = t - (uint32_t)__builtin_amdgcn_readlane((int)ex_g, ln);
+  int s = ln * SPL;
+  uint32_t first_cut = 0;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const uint32_t ci = (uint32_t)__builtin_amdgcn_readlane(
+        (int)(grp == 0 ? cnt[0][i] : (grp == 1 ? cnt[1][i] : cnt[2][i])), ln);
+    const uint32_t fc = (uint32_t)__builtin_amdgcn_readlane((int)fcut[i], ln);
+    if (s == ln * SPL + i) {
+      if (rank < ci) {
+        first_cut = fc;
+      } else {
+        rank -= ci;
+        ++s;
+      }
+    }
+  }
+  s = __builtin_amdgcn_readfirstlane(s);
+  rank = (uint32_t)__builtin_amdgcn_readfirstlane((int)rank);
+  first_cut = (uint32_t)__builtin_amdgcn_readfirstlane((int)first_cut);
+  const int32_t L = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
+  const int64_t seq_row0 = (int64_t)s * a.rows_per_seq;
+  // full slot number fi (in sequence order over the runs): its run and slot
+  auto full_slot = [&](uint32_t fi, int& r_o, int32_t& k_o) {
+    for (int r = 0; r < a.n_runs; ++r) {
+      int32_t rl, rh;
+      run_range(a, s, r, L, rl, rh);
+      const uint32_t nf = (uint32_t)full_slots(rl, rh, split);
+      if (fi < nf) {
+        r_o = r;
+        k_o = (int32_t)(((int64_t)rl + split - 1) / split) + (int32_t)fi;
+        return;
+      }
+      fi -= nf;
+    }
+    r_o = 0;
+    k_o = 0;
+  };
+  if (grp == 0) {
+    int r;
+    int32_t k;
+    full_slot(rank, r, k);
+    lo_out = k * split;
+    hi_out = lo_out + split;
+    row_out = seq_row0 + (int64_t)r * a.nspl + k;
+  } else if (grp == 2) {
+    int r;
+    int32_t k;
+    full_slot(first_cut + rank, r, k);
+    const uint32_t p = (it - all[0] - all[1]) % nsub;
+    lo_out = k * split + (int32_t)p * a.fine_tokens;
+    const int32_t e = lo_out + a.fine_tokens;
+    hi_out = e < k * split + split ? e : k * split + split;
+    row_out = seq_row0 + (int64_t)r * a.nspl + k + (int64_t)rank * (nsub - 1) + p;
+  } else {
+    // the rank-th partial slot: a run's partial slots are its first active
+    // slot (when partial) and its last (when partial and not the first)
+    uint32_t full_before = 0;
+    int32_t kk = 0, rr = 0, plo = 0, phi = 0;
+    uint32_t fb_here = 0;
+    for (int r = 0; r < a.n_runs; ++r) {
+      int32_t rl, rh;
+      run_range(a, s, r, L, rl, rh);
+      if (rh <= rl) continue;
+      const int32_t k0 = rl / split, k1 = (rh - 1) / split;
+      const int32_t kf0 = (int32_t)(((int64_t)rl + split - 1) / split), kf1 = rh / split;
+      const uint32_t nf = (uint32_t)full_slots(rl, rh, split);
+      const bool p0 = k0 < kf0 || k0 >= kf1;
+      const bool p1 = k1 != k0 && k1 >= kf1;
+      const uint32_t np = (p0 ? 1u : 0u) + (p1 ? 1u : 0u);
+      if (rank < np) {
+        const bool first = p0 && rank == 0;
+        kk = first ? k0 : k1;
+        rr = r;
+        plo = rl > kk * split ? rl : kk * split;
+        phi = rh < kk * split + split ? rh : kk * split + split;
+        // full slots of this run before slot kk
+        const int32_t fh = kk < kf0 ? 0 : (kk - kf0 < kf1 - kf0 ? kk - kf0 : kf1 - kf0);
+        fb_here = full_before + (uint32_t)(fh > 0 ? fh : 0);
+        break;
+      }
+      rank -= np;
+      full_before += nf;
+    }
+    const uint32_t cut_before = fb_here > first_cut ? fb_here - first_cut : 0u;
+    lo_out = plo;
+    hi_out = phi;
+    row_out = seq_row0 + (int64_t)rr * a.nspl + kk + (int64_t)cut_before * (nsub - 1);
+  }
+  s_out = s;
+  return true;
+}
+
 // Waves per SIMD and register budget of an instance: three waves (a ring
 // of at least two passes next to q, the running outputs and ~24
 // temporaries, in ~152 VGPRs) where they fit, else no bound on the waves
@@ -293,7 +456,16 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
   int s, kvh;
   int32_t lo, hi;
   int64_t prow;
-  if (a.items) {
+  if (a.self_plan) {
+    const uint32_t unit = blockIdx.x;
+    const uint32_t item = unit / (uint32_t)a.n_kv_heads;
+    kvh = (int)(unit - item * (uint32_t)a.n_kv_heads);
+    if (!self_plan_item(a, item, s, lo, hi, prow)) return;
+    s = __builtin_amdgcn_readfirstlane(s);
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    hi = __builtin_amdgcn_readfirstlane(hi);
+    if (lo >= hi) return;
+  } else if (a.items) {
     const uint32_t unit = blockIdx.x;
     if (unit >= a.hdr[0]) return;
     const uint32_t item = unit / (uint32_t)a.n_kv_heads;
@@ -487,7 +659,7 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
 // sequence).
 template <int HD, int BS, int G, int COMBO>
 hipError_t launch_split_instance(const AttnArgs& a, int64_t max_units, hipStream_t st) {
-  const dim3 grid = a.items ? dim3((unsigned)max_units)
+  const dim3 grid = (a.items || a.self_plan) ? dim3((unsigned)max_units)
                             : dim3((unsigned)a.n_kv_heads, (unsigned)(a.n_runs * a.nspl), (unsigned)a.n_seqs);
   hipLaunchKernelGGL((decode_split_kernel<HD, BS, G, COMBO>), grid, dim3(64), 0, st, a);
   return hipGetLastError();
@@ -495,25 +667,22 @@ hipError_t launch_split_instance(const AttnArgs& a, int64_t max_units, hipStream
 
 // Merge the partials of each (sequence, q head) by log-sum-exp:
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, lse = (M + log2 L) ln 2.
-// Four waves per workgroup, one lane per (q head, dim) output, so each load
-// is 256 contiguous bytes.  merge_split = 1: each wave merges all rows of
-// its own 64 outputs (256 outputs per workgroup).  merge_split = 4 (grids
-// too small to fill the device that way): the four waves share 64 outputs,
-// wave w merging rows w, w + 4, ..., and wave 0 combines the four results
-// in wave order through LDS.  Within a wave the rows go in order with a
-// running max, the loads of eight rows issued before their arithmetic.
-// Fixed order for a given shape, so results are deterministic.
-// A run's non-empty slots and their pieces hold one contiguous range of
-// rows, found from the run's bounds exactly as the plan pass places them.
-template <int HD, int NW>
+// A workgroup takes 256 consecutive (q head, dim) outputs of one sequence,
+// each lane four of them (16-byte loads, so a wave loads 1 KiB of a partial
+// row at once); its four waves share the rows (wave w takes rows w, w + 4,
+// ..., in order, with a running max, the loads of four rows issued before
+// their arithmetic) and wave 0 combines the four results in wave order
+// through LDS.  Fixed order for a given shape, so results are
+// deterministic.  A run's non-empty slots and their pieces hold one
+// contiguous range of rows, found from the run's bounds exactly as the plan
+// places them.
+template <int HD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
-  constexpr int kUnroll = 8, kWaves = 4;
-  __shared__ float part[3][kWaves - 1][64];
+  constexpr int kUnroll = 4, kWaves = 4;
+  __shared__ float part[kWaves - 1][6][64];
   const int s = blockIdx.y;
-  constexpr int nw = NW;  // waves per output group (merge_split): 1 or 4
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int grp = wv / nw, phase = wv - grp * nw;
-  const int idx = (blockIdx.x * (kWaves / nw) + grp) * 64 + lane;  // q head * HD + dim
+  const int idx = blockIdx.x * 256 + lane * 4;  // q head * HD + dim of the lane's first output
   const bool live = idx < a.n_q_heads * HD;
   const int h = live ? idx / HD : 0, d = live ? idx - h * HD : 0;
   const int32_t lim = clamp_seq_len(a.seq_lens[s], a.max_blocks, a.block_size);
@@ -524,19 +693,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     nfull += full_slots(rl, rh, a.split);
   }
   const int first_cut = nfull - (nfull < a.fine_per_seq ? nfull : a.fine_per_seq);
-  float m = -INFINITY, l = 0.f, acc = 0.f;
-  // merge (m2, l2, o2) into the running (m, l, acc); a partial that saw
-  // nothing (m2 = -inf) carries no weight, and an empty running value (m =
-  // -inf, l = acc = 0) is scaled by 2^-inf = 0
-  auto add = [&](float m2, float l2, float o2) {
+  float m = -INFINITY, l = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](float m2, float l2, const float (&o2)[4]) {
     if (m2 == -INFINITY) return;
     const float mn = fmaxf(m, m2);
     const float ca = fast_exp2(m - mn), cb = fast_exp2(m2 - mn);
-    acc = acc * ca + o2 * cb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * ca + o2[e] * cb;
     l = l * ca + l2 * cb;
     m = mn;
   };
-  // row(slot) = slot + (cut slots before it) * (nsub - 1)
   int full_before = 0;
   for (int r = 0; r < a.n_runs; ++r) {
     run_range(a, s, r, lim, rl, rh);
@@ -548,42 +715,47 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     full_before += nf;
     const int64_t row_a = (int64_t)s * a.rows_per_seq + (int64_t)r * a.nspl + k0 + (int64_t)cut0 * (a.nsub - 1);
     const int n_rows = k1 - k0 + 1 + (cut1 - cut0) * (a.nsub - 1);
-    for (int i0 = phase; live && i0 < n_rows; i0 += nw * kUnroll) {
+    for (int i0 = wv; live && i0 < n_rows; i0 += kWaves * kUnroll) {
       float2 ml[kUnroll];
-      float o[kUnroll];
+      float4 o[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         ml[u] = make_float2(-INFINITY, 0.f);
-        o[u] = 0.f;
-        const int i = i0 + nw * u;
+        o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int i = i0 + kWaves * u;
         if (i < n_rows) {
           const int64_t row = (row_a + i) * a.n_q_heads + h;
           ml[u] = *(const float2*)(a.part_ml + row * 2);
-          o[u] = a.part_o[row * HD + d];
+          o[u] = *(const float4*)(a.part_o + row * HD + d);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) add(ml[u].x, ml[u].y, o[u]);
+      for (int u = 0; u < kUnroll; ++u) {
+        const float ov[4] = {o[u].x, o[u].y, o[u].z, o[u].w};
+        add(ml[u].x, ml[u].y, ov);
+      }
     }
   }
-  if constexpr (nw > 1) {
-    if (phase > 0) {
-      part[0][phase - 1][lane] = m;
-      part[1][phase - 1][lane] = l;
-      part[2][phase - 1][lane] = acc;
-    }
-    __syncthreads();
-    if (phase > 0) return;
+  if (wv > 0) {
+    part[wv - 1][0][lane] = m;
+    part[wv - 1][1][lane] = l;
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves - 1; ++w2) add(part[0][w2][lane], part[1][w2][lane], part[2][w2][lane]);
+    for (int e = 0; e < 4; ++e) part[wv - 1][2 + e][lane] = acc[e];
   }
-  if (!live) return;
-  const int64_t oi = ((int64_t)s * a.n_q_heads + h) * HD + d;
+  __syncthreads();
+  if (wv > 0 || !live) return;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves - 1; ++w2) {
+    const float ov[4] = {part[w2][2][lane], part[w2][3][lane], part[w2][4][lane], part[w2][5][lane]};
+    add(part[w2][0][lane], part[w2][1][lane], ov);
+  }
+  float* orow = a.out + ((int64_t)s * a.n_q_heads + h) * HD + d;
   if (m == -INFINITY) {
-    a.out[oi] = 0.f;
+    *(float4*)orow = make_float4(0.f, 0.f, 0.f, 0.f);
     if (a.lse && d == 0) a.lse[(int64_t)s * a.n_q_heads + h] = -INFINITY;
   } else {
-    a.out[oi] = acc / l;
+    const float inv = 1.f / l;
+    *(float4*)orow = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
     if (a.lse && d == 0) a.lse[(int64_t)s * a.n_q_heads + h] = (m + __builtin_amdgcn_logf(l)) * kLn2;
   }
 }

@@ -283,16 +283,14 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
   a.part_o = (float*)((char*)ws + P.off_o);
   a.part_ml = (float*)((char*)ws + P.off_ml);
   a.err = (int32_t*)((char*)ws + P.off_err);
-  a.items = P.planned ? (const uint4*)((char*)ws + P.off_items) : nullptr;
+  // planned calls over few sequences derive the list in the split kernel
+  a.self_plan = P.planned && sh->n_seqs <= pkv::kSelfPlanMaxSeqs ? 1 : 0;
+  a.items = P.planned && !a.self_plan ? (const uint4*)((char*)ws + P.off_items) : nullptr;
   a.hdr = (uint32_t*)((char*)ws + P.off_hdr);
   a.nsub = P.nsub;
   a.fine_tokens = P.fine;
   a.fine_per_seq = P.fine_per_seq;
   a.rows_per_seq = P.rows_per_seq;
-  // The merge splits each output's rows over four waves when one wave per
-  // 64 outputs would give fewer than 512 workgroups (too few to fill the
-  // device); else each wave keeps its own outputs.  Depends on the shape only.
-  a.merge_split = (int64_t)sh->n_seqs * ((sh->n_q_heads * sh->head_dim + 255) / 256) < 512 ? 4 : 1;
   a.seqinfo = (uint4*)((char*)ws + P.off_seq);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -301,7 +299,7 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
       e = pkv::launch_zero_words(a.err, 1, s);
       if (e != hipSuccess) return device_fail(e, "clearing the error word");
     }
-    if (P.planned) {
+    if (a.items) {
       e = pkv::launch_decode_plan(a, s);
       if (e != hipSuccess) return device_fail(e, "decode plan launch");
     }

@@ -44,8 +44,10 @@ struct AttnArgs {
   uint32_t* hdr;
   uint4* seqinfo;
   int32_t nsub, fine_tokens, fine_per_seq;
+  // Planned calls with at most kSelfPlanMaxSeqs sequences skip the plan
+  // pass: each wave derives its own item of the same list (self_plan = 1).
+  int32_t self_plan;
   int64_t rows_per_seq;
-  int32_t merge_split;  // decode merge: waves sharing one group of outputs (1 or 4)
   int32_t n_q_total, max_q;
   int32_t nch;           // prefill: chunks each workgroup's window is split into
   // Pool layout [n_blocks][n_kv_heads][block_size][seg]: seg = bytes of one
@@ -107,6 +109,8 @@ __device__ inline void split_range(const AttnArgs& a, int s, int slot, int32_t l
   lo = (int32_t)x0;
   hi = (int32_t)x1;
 }
+
+constexpr int kSelfPlanMaxSeqs = 256;  // 4 sequences per lane of one wave
 
 // Number of split slots of a run [rl, rh) that it covers completely.
 __host__ __device__ inline int32_t full_slots(int32_t rl, int32_t rh, int32_t split) {
@@ -211,7 +215,7 @@ hipError_t launch_decode_plan(const AttnArgs& a, hipStream_t st);
 // Decode split pass: grid max_units (the host's bound on units) x 64 threads.
 hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int g,
                                int64_t max_units, hipStream_t st, bool* found);
-// Decode merge pass: grid (ceil(n_q_heads * head_dim / (256 / merge_split)), n_seqs), 256 threads.
+// Decode merge pass: grid (ceil(n_q_heads * head_dim / 256), n_seqs), 256 threads.
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
 // Prefill: workspace bytes a call needs (a multiple of 256, the last 256
 // bytes hold the checked-mode error word; 0 if none) and whether a kernel

@@ -374,3 +374,26 @@ def test_kv_map_at_the_run_limit(kind):
         else:
             pkv.paged_attn_prefill_window(d.q, d.cu_q, d.q_pos, d.k, d.v, d.table, d.lens, w.scale,
                                           int(np.max(np.diff(w.cu_q))), mode="kv_map", window=nine)
+
+
+@pytest.mark.parametrize("mode", ["causal", "kv_map"])
+def test_in_kernel_plan_equals_plan_pass(mode):
+    """Planned calls over at most 256 sequences derive the work list inside
+    the split kernel; larger ones write it with the plan pass first.  The
+    same 200 sequences, once alone (in-kernel list) and once as the first
+    200 of 300 (plan pass; same split size and cut slots), give bitwise
+    equal results, and both match the oracle."""
+    import torch
+
+    w = wgen.make_custom(seed=404, n_seqs=300, n_q_heads=16, n_kv_heads=8, head_dim=128, block_size=16,
+                         ctx=(1500, 6000), mode=mode, n_runs=3, hole_frac=0.05)
+    d = Dev(w)
+    win = d.window
+    kw = dict(mode=w.mode, split_tokens=1024)
+    out_all, lse_all = pkv.paged_attn_decode(d.q, d.k, d.v, d.table, d.lens, w.scale, window=win, **kw)
+    n = 200
+    out_sub, lse_sub = pkv.paged_attn_decode(d.q[:n], d.k, d.v, d.table[:n], d.lens[:n], w.scale,
+                                             window=None if win is None else win[:n], **kw)
+    assert torch.equal(out_sub, out_all[:n]) and torch.equal(lse_sub, lse_all[:n])
+    ro, rl = d.oracle()
+    compare(out_all.cpu().numpy(), lse_all.cpu().numpy(), ro, rl, tol_of(w), f"300 seqs {mode}")
