@@ -552,6 +552,15 @@ def run_prefill(args):
 
 
 def run_copy(args):
+    """copy_cells on 10,000 random overlapping moves over K and V pools of
+    2^17 blocks (8 kv heads x 16 slots x 512 B).  A step is one
+    kv_copy_cells call: the host plan (pinned memory), its asynchronous
+    upload and the device copies.  value: back-to-back calls, no
+    synchronization between them (the host plan of one call overlaps the
+    device copies of the one before), wall clock; also reported: one call at
+    a time (synchronized), the host plan alone and the device half alone
+    (HIP events around pkv_copy_cells_apply with the plan already on the
+    device)."""
     import torch
 
     import paged_kv_cache_table_amd as pkv
@@ -564,29 +573,67 @@ def run_copy(args):
     v = torch.zeros_like(k)
     changed = int(ms_.moves[:, 2].sum())  # rows the moves name (a row moved twice counts twice)
     row = w.row_bytes("k") + w.row_bytes("v")
+    ws = torch.empty(pkv.copy_cells_workspace_bytes(ms_.moves, k, v), dtype=torch.uint8, device="cuda")
+    n_rows = w.n_pool_blocks * w.block_size
+
+    def call():
+        pkv.kv_copy_cells(k, v, ms_.moves, workspace=ws)
+
     for _ in range(args.warmup):
-        pkv.kv_copy_cells(k, v, ms_.moves)
+        call()
     torch.cuda.synchronize()
-    # the call plans on the host and waits for its plan upload; the copy kernels
-    # are queued when it returns, so wall clock to the next synchronize covers
-    # plan + upload + device copies
-    t_wall = []
+    # one call at a time
+    t_single = []
     for _ in range(args.steps):
         t0 = time.perf_counter()
-        pkv.kv_copy_cells(k, v, ms_.moves)
+        call()
         torch.cuda.synchronize()
-        t_wall.append(time.perf_counter() - t0)
+        t_single.append(time.perf_counter() - t0)
+    # host plan alone
+    t_plan = []
+    for _ in range(args.steps):
+        t0 = time.perf_counter()
+        info, plan_h = pkv.copy_cells_plan(ms_.moves, n_rows)
+        t_plan.append(time.perf_counter() - t0)
+    # device half alone
+    plan_d = plan_h[: info.n_words].cuda()
+    stage = torch.empty(pkv.copy_cells_stage_bytes(info, k, v), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    dev_ms = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pkv.copy_cells_apply(k, v, info, plan_d, stage)
+        e1.record()
+        torch.cuda.synchronize()
+        dev_ms.append(e0.elapsed_time(e1))
+    # back to back, last
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
     moved = 2 * changed * row  # each moved row read once and written once
-    wall = float(np.mean(t_wall))
+    dev = float(np.mean(dev_ms))
+    dev_bytes = 2 * (info.n_scatter + info.n_gather) * row  # rows read and written by the device half
     return {
         "metric": "copy_cells: rows moved per second (bit-exact, sequential order_moves semantics)",
         "value": round(changed / wall, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bytes", "data": "synthetic",
         "config": {"workload": "10,000 random overlapping moves (len 1..32) on K and V pools of 2^17 blocks x 16 "
-                               "slots x 8 kv heads x 512 B; host plan + upload + device copies, wall clock",
-                   "moved_rows": changed, "min_bytes": moved},
+                               "slots x 8 kv heads x 512 B; back-to-back kv_copy_cells calls (host plan + "
+                               "asynchronous upload + device copies), wall clock",
+                   "moved_rows": changed, "min_bytes": moved, "plan_words": int(info.n_words),
+                   "staged_rows": int(info.n_gather), "written_rows": int(info.n_scatter)},
         "GBps_min_bytes_wall": round(moved / wall / 1e9, 2),
+        "single_call_ms": round(float(np.mean(t_single)) * 1e3, 4),
+        "host_plan_ms": round(float(np.mean(t_plan)) * 1e3, 4),
+        "device_ms": round(dev, 4),
+        "roofline": {"bound": "hbm", "kernel": "copy_rows_kernel (gather + scatter, both pools)",
+                     "achieved": round(dev_bytes / (dev * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dev_bytes / (dev * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
     }
 
 

@@ -39,11 +39,11 @@
  *    single-threading contract"): one caller mutates a pool at a time;
  *    calls on one stream are ordered.
  *  - Graph capture: the decode calls, pkv_paged_attn_prefill_window,
- *    pkv_kv_store, pkv_cow_apply and the int4 codec only launch kernels on
- *    `stream` (no synchronization, allocation or memset), so they can be
- *    captured into a HIP graph and replayed.  With PKV_FLAG_CHECKED they
- *    wait for the stream and cannot; pkv_kv_copy_cells plans on the host and
- *    waits for its upload, so it cannot either.
+ *    pkv_kv_store, pkv_cow_apply, pkv_copy_cells_apply and the int4 codec
+ *    only launch kernels on `stream` (no synchronization, allocation or
+ *    memset), so they can be captured into a HIP graph and replayed.  With
+ *    PKV_FLAG_CHECKED they wait for the stream and cannot; pkv_kv_copy_cells
+ *    uploads its plan from the host, so it cannot either.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -242,25 +242,81 @@ pkv_status pkv_paged_attn_prefill_window(const pkv_shape* shape, int32_t n_q_tot
  * count. */
 pkv_status pkv_order_moves(const int32_t* moves, int32_t n, int32_t* order_out, int32_t* n_out);
 
-/* Workspace for pkv_kv_copy_cells with these moves (an upper bound);
- * row_bytes_* = bytes of one token cell (all kv heads) of each pool. */
+/* copy_cells in two halves, so that the host work and the device work can
+ * be placed (and overlapped) by the caller, and the device half captured
+ * into a HIP graph:
+ *  - pkv_copy_cells_plan (host only, no device calls): orders the moves and
+ *    reduces them to a plan written into caller memory (any host memory;
+ *    pinned memory lets the caller upload it asynchronously);
+ *  - the caller copies the plan's n_words int32 words to device memory;
+ *  - pkv_copy_cells_apply (device only: kernels on `stream`, nothing else):
+ *    moves the rows.
+ * Plan kinds: when no destination of a move overlaps another destination or
+ * any source (every compaction the block pool plans), every application
+ * order gives the same bytes and the plan is the moves themselves (kind 1:
+ * [n_moves][3] (src, dst, len), then the n_moves + 1 prefix sums of the
+ * lengths).  Otherwise the ordered moves are replayed on the host into the
+ * final source of every changed row (kind 2: [n_gather][2] (source row,
+ * stage slot) for rows that are read and also overwritten, then
+ * [n_scatter][2] (row, source row or -(stage slot + 1))); the device first
+ * copies the gathered rows into a stage, then writes every changed row. */
+typedef struct {
+  int32_t kind;       /* 0: nothing to copy; 1: disjoint runs; 2: staged rows */
+  int32_t n_moves;    /* kind 1: runs (moves with len > 0 and src != dst)  */
+  int32_t total_rows; /* kind 1: rows the runs copy                          */
+  int32_t n_gather;   /* kind 2: rows copied into the stage first            */
+  int32_t n_scatter;  /* kind 2: rows written                                */
+  int32_t reserved;
+  int64_t n_words;    /* int32 words of the plan                             */
+} pkv_copy_plan;
+
+/* Words of the plan buffer pkv_copy_cells_plan needs for these moves: room
+ * for the plan and for the planner's working arrays, so that planning
+ * allocates nothing (0 when there is nothing to move or on bad input). */
+int64_t pkv_copy_cells_plan_words(const int32_t* moves, int32_t n);
+
+/* Host only.  moves: host int32 [n][3] in pool rows; every effective move
+ * must lie inside [0, n_pool_rows) or the call is refused.  plan: host int32
+ * [plan_words], 8-byte aligned, at least pkv_copy_cells_plan_words; the
+ * call works in it and leaves the plan in its first info->n_words words;
+ * *info receives the kind and the counts.  No global state and no
+ * allocation: safe to call from any thread, and callers that keep one
+ * buffer (pinned, say) reuse it without page faults. */
+pkv_status pkv_copy_cells_plan(const int32_t* moves, int32_t n, int64_t n_pool_rows, int32_t* plan,
+                               int64_t plan_words, pkv_copy_plan* info);
+
+/* Device stage bytes pkv_copy_cells_apply needs for this plan (kind 2:
+ * n_gather rows of each pool; else 0). */
+size_t pkv_copy_cells_stage_bytes(const pkv_copy_plan* info, int64_t row_bytes_k, int64_t row_bytes_v);
+
+/* Device only.  Applies a plan to k_pool and, if not NULL, v_pool (both
+ * [n_pool_blocks][n_kv_heads][block_size][seg], seg_bytes_* a multiple of
+ * 4).  plan: device int32 [info->n_words], the words pkv_copy_cells_plan
+ * wrote.  stage: device, pkv_copy_cells_stage_bytes bytes, 16-byte aligned
+ * (may be NULL for kind 0 and 1).  Launches kernels on `stream` only (no
+ * allocation, copy or synchronization), so it can be captured into a HIP
+ * graph; a captured apply moves the rows again on every replay.  Rows or
+ * stage slots in the device plan outside the pool or the stage are skipped
+ * (the plan is device data the host does not read back). */
+pkv_status pkv_copy_cells_apply(void* k_pool, void* v_pool, int32_t n_pool_blocks, int32_t block_size,
+                                int32_t n_kv_heads, int64_t seg_bytes_k, int64_t seg_bytes_v,
+                                const pkv_copy_plan* info, const int32_t* plan, void* stage,
+                                size_t stage_bytes, void* stream);
+
+/* Workspace for pkv_kv_copy_cells with these moves (an upper bound: the
+ * plan and the stage); row_bytes_* = bytes of one token cell (all kv heads)
+ * of each pool. */
 size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t row_bytes_k,
                                       int64_t row_bytes_v);
 
-/* Apply moves (host int32 [n][3], in pool rows) to k_pool and, if not NULL,
- * v_pool, bit-exact.  Both pools are [n_pool_blocks][n_kv_heads][block_size]
- * [seg] (device; seg_bytes_k / seg_bytes_v bytes per token per kv head, a
- * multiple of 4); a row is one slot of every kv head, so a move carries all
- * kv heads of its tokens.  The host plans the moves (order_moves, then the
- * final source of every changed row) and writes the plan into one of two
- * pinned host buffers that the library keeps per device (allocated on first
- * use, grown to the largest plan seen, kept until the process ends;
- * concurrent calls take turns on them), from which it is copied into the
- * workspace on `stream`.  `moves` may be freed on return; the upload and the
- * copies run asynchronously on `stream`.  A call waits only for the previous
- * upload out of the same pinned buffer, never for the rest of the stream.
- * Every move must lie inside [0, n_pool_blocks * block_size) or the call is
- * refused untouched. */
+/* Plan, upload and apply in one call: moves (host int32 [n][3]) are planned
+ * into memory the call allocates and frees on the host, the plan is copied
+ * into the front of `workspace` on `stream` and the call waits for the
+ * stream (so the plan's host memory can be freed), then the rows are moved
+ * as by pkv_copy_cells_apply with the rest of the workspace as the stage
+ * (asynchronously).  `moves` may be freed on return.  Not capturable;
+ * callers that plan ahead, overlap the host plan with device work or
+ * capture use the two halves. */
 pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, int32_t block_size,
                              int32_t n_kv_heads, int64_t seg_bytes_k, int64_t seg_bytes_v,
                              const int32_t* moves, int32_t n, void* workspace,

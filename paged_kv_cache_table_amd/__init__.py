@@ -42,6 +42,10 @@ EXPORTS = (
     "pkv_prefill_workspace_bytes",
     "pkv_paged_attn_prefill_window",
     "pkv_order_moves",
+    "pkv_copy_cells_plan_words",
+    "pkv_copy_cells_plan",
+    "pkv_copy_cells_stage_bytes",
+    "pkv_copy_cells_apply",
     "pkv_copy_cells_workspace_bytes",
     "pkv_kv_copy_cells",
     "pkv_kv_store",
@@ -116,6 +120,10 @@ def lib() -> ctypes.CDLL:
         "pkv_paged_attn_prefill_window": (I32, [SH, I32, I32, P, P, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]),
         "pkv_order_moves": (I32, [P, I32, P, P]),
         "pkv_copy_cells_workspace_bytes": (SZ, [P, I32, I64, I64]),
+        "pkv_copy_cells_plan_words": (I64, [P, I32]),
+        "pkv_copy_cells_plan": (I32, [P, I32, I64, P, I64, P]),
+        "pkv_copy_cells_stage_bytes": (SZ, [P, I64, I64]),
+        "pkv_copy_cells_apply": (I32, [P, P, I32, I32, I32, I64, I64, P, P, P, SZ, P]),
         "pkv_kv_copy_cells": (I32, [P, P, I32, I32, I32, I64, I64, P, I32, P, SZ, P]),
         "pkv_kv_store": (I32, [SH, I32, I32, P, P, P, P, P, P, P, P, P]),
         "pkv_pool_create": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(P)]),
@@ -433,16 +441,16 @@ def order_moves(moves) -> list:
     return order[: n_out.value].tolist()
 
 
-def kv_copy_cells(k_pool, v_pool, moves, workspace=None):
-    """Apply (src, dst, len) row moves (host int32 array [n, 3]) to both pools
-    in order_moves order, bit-exact.  Pools are [n_blocks, n_kv_heads,
-    block_size, W]; a row is one slot of every kv head."""
-    import numpy as np
+class CopyPlan(ctypes.Structure):
+    """pkv_copy_plan: what pkv_copy_cells_plan wrote (kind 0 nothing, 1
+    disjoint runs, 2 staged rows; counts; plan words)."""
 
-    torch = _torch()
-    _on_one_gpu(k_pool, v_pool, workspace)
-    mv = np.ascontiguousarray(np.asarray(moves, dtype=np.int32).reshape(-1, 3))
-    n = mv.shape[0]
+    _fields_ = [("kind", ctypes.c_int32), ("n_moves", ctypes.c_int32), ("total_rows", ctypes.c_int32),
+                ("n_gather", ctypes.c_int32), ("n_scatter", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_words", ctypes.c_int64)]
+
+
+def _pool_geometry(k_pool, v_pool):
     for t in (k_pool, v_pool):
         if t is not None and (not t.is_contiguous() or t.dim() != 4):
             raise TypeError("pools must be contiguous [n_blocks, n_kv_heads, block_size, W]")
@@ -453,11 +461,83 @@ def kv_copy_cells(k_pool, v_pool, moves, workspace=None):
         if tuple(v_pool.shape[:3]) != (nb, hkv, bs):
             raise ValueError("K and V pools must agree on (n_blocks, n_kv_heads, block_size)")
         seg_v = v_pool.shape[3] * v_pool.element_size()
-    need = int(lib().pkv_copy_cells_workspace_bytes(mv.ctypes.data, n, seg_k * hkv, seg_v * hkv))
-    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=k_pool.device)
-    _check(lib().pkv_kv_copy_cells(_ptr(k_pool), _ptr(v_pool), nb, bs, hkv, seg_k, seg_v, mv.ctypes.data, n,
-                                   _ptr(ws), ws.numel(), _stream(k_pool)))
+    return nb, hkv, bs, seg_k, seg_v
+
+
+def _moves_array(moves):
+    import numpy as np
+
+    return np.ascontiguousarray(np.asarray(moves, dtype=np.int32).reshape(-1, 3))
+
+
+def copy_cells_plan(moves, n_pool_rows: int, pin_memory: bool = True):
+    """pkv_copy_cells_plan (host): returns (info, plan), plan a host int32
+    tensor (pinned when pin_memory, so it can be uploaded asynchronously)
+    whose first info.n_words words are the plan."""
+    torch = _torch()
+    mv = _moves_array(moves)
+    n = mv.shape[0]
+    words = int(lib().pkv_copy_cells_plan_words(mv.ctypes.data, n))
+    plan = torch.empty(max(words, 1), dtype=torch.int32, pin_memory=pin_memory)
+    info = CopyPlan()
+    _check(lib().pkv_copy_cells_plan(mv.ctypes.data, n, int(n_pool_rows), plan.data_ptr(), words,
+                                     ctypes.byref(info)))
+    return info, plan
+
+
+def copy_cells_stage_bytes(info: CopyPlan, k_pool, v_pool) -> int:
+    _, hkv, _, seg_k, seg_v = _pool_geometry(k_pool, v_pool)
+    return int(lib().pkv_copy_cells_stage_bytes(ctypes.byref(info), seg_k * hkv, seg_v * hkv))
+
+
+def copy_cells_apply(k_pool, v_pool, info: CopyPlan, plan, stage=None):
+    """pkv_copy_cells_apply (device only, capturable): plan is a device int32
+    tensor holding the info.n_words words pkv_copy_cells_plan wrote; stage a
+    device uint8 tensor of copy_cells_stage_bytes bytes (kind 2)."""
+    torch = _torch()
+    _on_one_gpu(k_pool, v_pool, plan, stage)
+    nb, hkv, bs, seg_k, seg_v = _pool_geometry(k_pool, v_pool)
+    _sized(plan, "plan", int(info.n_words), torch.int32)
+    need = int(lib().pkv_copy_cells_stage_bytes(ctypes.byref(info), seg_k * hkv, seg_v * hkv))
+    _sized(stage, "stage", need, torch.uint8)
+    _check(lib().pkv_copy_cells_apply(_ptr(k_pool), _ptr(v_pool), nb, bs, hkv, seg_k, seg_v, ctypes.byref(info),
+                                      _ptr(plan), _ptr(stage), 0 if stage is None else stage.numel(),
+                                      _stream(k_pool)))
+
+
+def kv_copy_cells(k_pool, v_pool, moves, workspace=None):
+    """Apply (src, dst, len) row moves (host int32 array [n, 3]) to both pools
+    in order_moves order, bit-exact.  Pools are [n_blocks, n_kv_heads,
+    block_size, W]; a row is one slot of every kv head.  The plan is made on
+    the host into pinned memory, copied to the device asynchronously on the
+    current stream (the front of `workspace`, a device uint8 tensor, when
+    given) and applied there; nothing waits for the device."""
+    torch = _torch()
+    _on_one_gpu(k_pool, v_pool, workspace)
+    nb, hkv, bs, seg_k, seg_v = _pool_geometry(k_pool, v_pool)
+    info, plan_h = copy_cells_plan(moves, nb * bs)
+    if info.kind == 0:
+        return k_pool, v_pool
+    words = int(info.n_words)
+    plan_bytes = (words * 4 + 255) // 256 * 256
+    stage_bytes = int(lib().pkv_copy_cells_stage_bytes(ctypes.byref(info), seg_k * hkv, seg_v * hkv))
+    if workspace is None:
+        workspace = torch.empty(plan_bytes + max(stage_bytes, 256), dtype=torch.uint8, device=k_pool.device)
+    _sized(workspace, "workspace", plan_bytes + stage_bytes, torch.uint8)
+    plan_d = workspace[: words * 4].view(torch.int32)
+    plan_d.copy_(plan_h[:words], non_blocking=True)
+    stage = workspace[plan_bytes:]
+    _check(lib().pkv_copy_cells_apply(_ptr(k_pool), _ptr(v_pool), nb, bs, hkv, seg_k, seg_v, ctypes.byref(info),
+                                      _ptr(plan_d), _ptr(stage), stage.numel(), _stream(k_pool)))
     return k_pool, v_pool
+
+
+def copy_cells_workspace_bytes(moves, k_pool, v_pool) -> int:
+    """pkv_copy_cells_workspace_bytes: an upper bound on what kv_copy_cells
+    (or pkv_kv_copy_cells) needs for these moves."""
+    mv = _moves_array(moves)
+    _, hkv, _, seg_k, seg_v = _pool_geometry(k_pool, v_pool)
+    return int(lib().pkv_copy_cells_workspace_bytes(mv.ctypes.data, mv.shape[0], seg_k * hkv, seg_v * hkv))
 
 
 # ---------------------------------------------------------------------------

@@ -18,7 +18,7 @@ namespace pkv {
 // so no division runs per word.
 template <typename W>
 __global__ __launch_bounds__(256) void copy_rows_kernel(int phase, PoolGeom g, unsigned char* stage,
-                                                        const int32_t* pairs, int32_t n_pairs) {
+                                                        int32_t n_stage, const int32_t* pairs, int32_t n_pairs) {
   const int lane = threadIdx.x & 63;
   const int32_t p = (int32_t)blockIdx.x * 4 + (int32_t)(threadIdx.x >> 6);  // wave-uniform
   if (p >= n_pairs) return;
@@ -32,6 +32,10 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(int phase, PoolGeom g, u
     return g.base + (int64_t)blk * block_bytes + (int64_t)slot * g.seg_bytes;
   };
   const int32_t x = pairs[2 * p], y = pairs[2 * p + 1];
+  // the plan is device data: a pair naming a row outside the pool or a slot
+  // outside the stage is skipped
+  if (x < 0 || x >= g.n_rows) return;
+  if (phase == 1 ? (y < 0 || y >= n_stage) : (y >= g.n_rows || (y < 0 && -(int64_t)y - 1 >= n_stage))) return;
   int32_t h = lane / per_seg, c = lane - h * per_seg;
   const int32_t dh = 64 / per_seg, dc = 64 - dh * per_seg;
   if (phase == 1) {
@@ -102,8 +106,11 @@ __global__ __launch_bounds__(256) void copy_runs_kernel(PoolGeom g, const int32_
       }
       const int64_t o = r - cum[lo];
       const int64_t sr = moves[3 * lo] + o, dr = moves[3 * lo + 1] + o;
-      so = (sr / g.block_size) * block_bytes + (sr % g.block_size) * g.seg_bytes;
-      dof = (dr / g.block_size) * block_bytes + (dr % g.block_size) * g.seg_bytes;
+      // the plan is device data: rows outside the pool are skipped
+      if (sr >= 0 && sr < g.n_rows && dr >= 0 && dr < g.n_rows) {
+        so = (sr / g.block_size) * block_bytes + (sr % g.block_size) * g.seg_bytes;
+        dof = (dr / g.block_size) * block_bytes + (dr % g.block_size) * g.seg_bytes;
+      }
     }
     src_off[threadIdx.x] = so;
     dst_off[threadIdx.x] = dof;
@@ -147,17 +154,17 @@ hipError_t launch_copy_runs(const PoolGeom& pool, const int32_t* moves, const in
   return hipGetLastError();
 }
 
-hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stage,
+hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stage, int32_t n_stage,
                             const int32_t* pairs, int32_t n_pairs, hipStream_t st) {
   if (n_pairs <= 0) return hipSuccess;
   const bool wide = (pool.seg_bytes % 16) == 0;
   const int64_t blocks = ((int64_t)n_pairs + 3) / 4;  // one wave per pair
   if (wide)
     hipLaunchKernelGGL(copy_rows_kernel<uint4>, dim3((unsigned)blocks), dim3(256), 0, st, phase,
-                       pool, stage, pairs, n_pairs);
+                       pool, stage, n_stage, pairs, n_pairs);
   else
     hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st, phase,
-                       pool, stage, pairs, n_pairs);
+                       pool, stage, n_stage, pairs, n_pairs);
   return hipGetLastError();
 }
 

@@ -1,14 +1,12 @@
 // C ABI of the paged-attention library: argument validation, dispatch over
-// (head_dim, block_size, group, formats), split planning, order_moves and
-// the copy_cells plan.  Every host-checkable condition is checked before
+// (head_dim, block_size, group, formats) and split planning (order_moves and
+// the copy_cells plan live in copy_plan.cpp).  Every host-checkable condition is checked before
 // the first launch, so a refused call leaves outputs and pools untouched.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <map>
-#include <mutex>
 #include <string>
 #include <vector>
 
@@ -319,167 +317,6 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
   return ok();
 }
 
-// order_moves: indices of the effective moves, upward moves (dst > src) by
-// descending src then descending dst, then downward moves by ascending src
-// then ascending dst; ties by input index.
-// Stable LSD radix sort of (key, index) pairs by key, 8 bits per pass;
-// passes whose digit is the same for every key are skipped.
-void radix_sort_pairs(std::vector<std::pair<uint64_t, int32_t>>* v) {
-  // host buffers keep their capacity between calls (no page faults in
-  // steady state); thread-local, so concurrent callers do not share them
-  static thread_local std::vector<std::pair<uint64_t, int32_t>> tmp;
-  tmp.resize(v->size());
-  uint64_t all_or = 0, all_and = ~0ull;
-  for (const auto& x : *v) {
-    all_or |= x.first;
-    all_and &= x.first;
-  }
-  for (int shift = 0; shift < 64; shift += 8) {
-    if ((((all_or ^ all_and) >> shift) & 0xFF) == 0) continue;  // constant digit
-    size_t count[257] = {0};
-    for (const auto& x : *v) ++count[((x.first >> shift) & 0xFF) + 1];
-    for (int b = 0; b < 256; ++b) count[b + 1] += count[b];
-    for (const auto& x : *v) tmp[count[(x.first >> shift) & 0xFF]++] = x;
-    v->swap(tmp);
-  }
-}
-
-// order_moves: moves with dst > src first, by src then dst descending; then
-// moves with dst < src, by src then dst ascending; ties keep input order.
-// Moves with len <= 0 or src == dst are dropped.  (Keys are built so that an
-// ascending stable sort gives that order: flipping the sign bit maps int32
-// onto uint32 in order, and 2^32 - 1 - x reverses it.)
-// The result lives in a thread-local buffer, valid until the next call.
-const std::vector<int32_t>& order_moves_impl(const int32_t* mv, int32_t n) {
-  static thread_local std::vector<std::pair<uint64_t, int32_t>> up, down;
-  static thread_local std::vector<int32_t> o;
-  up.clear();
-  down.clear();
-  for (int32_t i = 0; i < n; ++i) {
-    const int32_t s = mv[3 * i], d = mv[3 * i + 1], len = mv[3 * i + 2];
-    if (len <= 0 || d == s) continue;
-    const uint64_t us = (uint32_t)s ^ 0x80000000u, ud = (uint32_t)d ^ 0x80000000u;
-    if (d > s) up.push_back({((0xFFFFFFFFull - us) << 32) | (0xFFFFFFFFull - ud), i});
-    else down.push_back({(us << 32) | ud, i});
-  }
-  radix_sort_pairs(&up);
-  radix_sort_pairs(&down);
-  o.clear();
-  for (const auto& x : up) o.push_back(x.second);
-  for (const auto& x : down) o.push_back(x.second);
-  return o;
-}
-
-// The effective moves (len > 0, src != dst) as (src, dst, len), and whether
-// they are disjoint: destinations do not overlap each other and no
-// destination overlaps any source.  Then every application order gives the
-// same bytes and all rows can be copied at once.
-bool disjoint_moves(const int32_t* mv, int32_t n, std::vector<int32_t>* eff) {
-  eff->clear();
-  for (int32_t i = 0; i < n; ++i) {
-    const int64_t s = mv[3 * i], d = mv[3 * i + 1], len = mv[3 * i + 2];
-    if (len <= 0 || s == d) continue;
-    if (s < d + len && d < s + len) return false;  // a move overlapping itself (a slide)
-    eff->insert(eff->end(), {(int32_t)s, (int32_t)d, (int32_t)len});
-  }
-  const size_t m = eff->size() / 3;
-  static thread_local std::vector<std::pair<int64_t, int64_t>> src, dst;
-  src.clear();
-  dst.clear();
-  for (size_t i = 0; i < m; ++i) {
-    const int64_t s = (*eff)[3 * i], d = (*eff)[3 * i + 1], len = (*eff)[3 * i + 2];
-    src.push_back({s, s + len});
-    dst.push_back({d, d + len});
-  }
-  std::sort(dst.begin(), dst.end());
-  for (size_t i = 1; i < dst.size(); ++i)
-    if (dst[i].first < dst[i - 1].second) return false;  // two destinations overlap
-  std::sort(src.begin(), src.end());
-  // destinations are disjoint and sorted; a source overlaps one iff the
-  // first destination ending after the source's start begins before its end
-  size_t j = 0;
-  for (const auto& sr : src) {
-    while (j < dst.size() && dst[j].second <= sr.first) ++j;
-    if (j < dst.size() && dst[j].first < sr.second) return false;
-  }
-  return true;
-}
-
-// Pinned host staging for plan uploads: grown to the largest plan so far and
-// kept until the process ends; one upload at a time.
-// Pinned staging for host -> device plan uploads: two buffers per device,
-// used in turn, each with an event recorded after its copy, so a call waits
-// only for the previous upload out of the same buffer (never for the rest of
-// the stream) before refilling it.  Allocated on first use, grown to the
-// largest plan seen, kept until the process ends; the mutex makes
-// concurrent callers take turns.
-struct StageSet {
-  void* buf[2] = {nullptr, nullptr};
-  size_t bytes[2] = {0, 0};
-  hipEvent_t ev[2] = {nullptr, nullptr};
-  bool pending[2] = {false, false};
-  int next = 0;
-};
-std::mutex g_stage_mu;
-std::map<int, StageSet> g_stages;
-
-// A pinned host buffer of at least `bytes`, held (with the mutex) until
-// commit() sends it to the device.
-class StagedUpload {
- public:
-  hipError_t begin(size_t bytes) {
-    lock_ = std::unique_lock<std::mutex>(g_stage_mu);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    set_ = &g_stages[dev];
-    i_ = set_->next;
-    set_->next ^= 1;
-    if (set_->pending[i_]) {
-      e = hipEventSynchronize(set_->ev[i_]);
-      if (e != hipSuccess) return e;
-      set_->pending[i_] = false;
-    }
-    if (!set_->ev[i_]) {
-      e = hipEventCreateWithFlags(&set_->ev[i_], hipEventDisableTiming);
-      if (e != hipSuccess) {
-        set_->ev[i_] = nullptr;
-        return e;
-      }
-    }
-    if (set_->bytes[i_] < bytes) {
-      if (set_->buf[i_]) (void)hipHostFree(set_->buf[i_]);
-      set_->buf[i_] = nullptr;
-      set_->bytes[i_] = 0;
-      const size_t want = std::max(bytes, (size_t)1 << 20);
-      e = hipHostMalloc(&set_->buf[i_], want, hipHostMallocDefault);
-      if (e != hipSuccess) {
-        set_->buf[i_] = nullptr;
-        return e;
-      }
-      set_->bytes[i_] = want;
-    }
-    return hipSuccess;
-  }
-  void* host() const { return set_->buf[i_]; }
-  // Copies the first `bytes` of the buffer to `dst` on `st` (asynchronous).
-  hipError_t commit(void* dst, size_t bytes, hipStream_t st) {
-    hipError_t e = hipSuccess;
-    if (bytes) {
-      e = hipMemcpyAsync(dst, set_->buf[i_], bytes, hipMemcpyHostToDevice, st);
-      if (e == hipSuccess) e = hipEventRecord(set_->ev[i_], st);
-      if (e == hipSuccess) set_->pending[i_] = true;
-    }
-    lock_.unlock();
-    return e;
-  }
-
- private:
-  std::unique_lock<std::mutex> lock_;
-  StageSet* set_ = nullptr;
-  int i_ = 0;
-};
-
 }  // namespace
 
 namespace pkv_host {
@@ -605,174 +442,6 @@ pkv_status pkv_paged_attn_prefill_window(const pkv_shape* sh, int32_t n_q_total,
   hipError_t e = pkv::launch_prefill(a, P.combo, sh->head_dim, sh->block_size, P.g, s, &found);
   if (e != hipSuccess) return device_fail(e, "prefill launch");
   return finish_checked(a, s);
-}
-
-pkv_status pkv_order_moves(const int32_t* moves, int32_t n, int32_t* order_out, int32_t* n_out) {
-  if (n < 0) return fail(PKV_E_ARG, "negative move count %d", n);
-  if (n > 0 && (!moves || !order_out)) return fail(PKV_E_ARG, "moves and order_out must be non-NULL");
-  if (!n_out) return fail(PKV_E_ARG, "n_out is NULL");
-  const std::vector<int32_t>& o = order_moves_impl(moves, n);
-  std::copy(o.begin(), o.end(), order_out);
-  *n_out = (int32_t)o.size();
-  return ok();
-}
-
-size_t pkv_copy_cells_workspace_bytes(const int32_t* moves, int32_t n, int64_t row_bytes_k,
-                                      int64_t row_bytes_v) {
-  if (n < 0 || (n > 0 && !moves) || row_bytes_k <= 0 || row_bytes_v < 0) return 0;
-  static thread_local std::vector<int32_t> eff;
-  if (disjoint_moves(moves, n, &eff))  // moves and their prefix sums only
-    return align_up((eff.size() + eff.size() / 3 + 1) * sizeof(int32_t), 256) + 256;
-  int64_t rows = 0;
-  for (int32_t i = 0; i < n; ++i)
-    if (moves[3 * i + 2] > 0 && moves[3 * i] != moves[3 * i + 1]) rows += moves[3 * i + 2];
-  return align_up((size_t)rows * 2 * sizeof(int32_t) * 2, 256) +
-         align_up((size_t)rows * (size_t)row_bytes_k, 256) +
-         align_up((size_t)rows * (size_t)row_bytes_v, 256) + 256;
-}
-
-pkv_status pkv_kv_copy_cells(void* k_pool, void* v_pool, int32_t n_pool_blocks, int32_t block_size,
-                             int32_t n_kv_heads, int64_t seg_bytes_k, int64_t seg_bytes_v,
-                             const int32_t* moves, int32_t n, void* ws, size_t ws_bytes,
-                             void* stream) {
-  if (!k_pool) return fail(PKV_E_ARG, "k_pool is NULL");
-  if (n < 0) return fail(PKV_E_ARG, "negative move count %d", n);
-  if (n > 0 && !moves) return fail(PKV_E_ARG, "moves is NULL");
-  if (n_pool_blocks <= 0 || block_size <= 0 || n_kv_heads <= 0)
-    return fail(PKV_E_ARG, "n_pool_blocks %d, block_size %d and n_kv_heads %d must be positive",
-                n_pool_blocks, block_size, n_kv_heads);
-  const int64_t n_pool_rows = (int64_t)n_pool_blocks * block_size;
-  if (n_pool_rows > INT32_MAX)
-    return fail(PKV_E_ARG, "%lld pool rows exceed 2^31 - 1", (long long)n_pool_rows);
-  if (seg_bytes_k <= 0 || seg_bytes_k % 4)
-    return fail(PKV_E_ARG, "seg_bytes_k %lld must be a positive multiple of 4", (long long)seg_bytes_k);
-  if (v_pool && (seg_bytes_v <= 0 || seg_bytes_v % 4))
-    return fail(PKV_E_ARG, "seg_bytes_v %lld must be a positive multiple of 4", (long long)seg_bytes_v);
-  int64_t lo = INT64_MAX, hi = -1;
-  for (int32_t i = 0; i < n; ++i) {
-    const int64_t s = moves[3 * i], d = moves[3 * i + 1], len = moves[3 * i + 2];
-    if (len <= 0 || s == d) continue;
-    if (s < 0 || d < 0 || s + len > n_pool_rows || d + len > n_pool_rows)
-      return fail(PKV_E_ARG, "move %d (src %lld, dst %lld, len %lld) leaves [0, %lld)", i,
-                  (long long)s, (long long)d, (long long)len, (long long)n_pool_rows);
-    lo = std::min(lo, std::min(s, d));
-    hi = std::max(hi, std::max(s, d) + len);
-  }
-  const std::vector<int32_t>& order = order_moves_impl(moves, n);
-  if (order.empty()) return ok();
-  hipStream_t st = (hipStream_t)stream;
-  static thread_local std::vector<int32_t> eff;
-  if (disjoint_moves(moves, n, &eff)) {
-    // No destination touches a source: copy every run at once.  Upload:
-    // the moves, then the prefix sums of their lengths.
-    const int32_t m = (int32_t)(eff.size() / 3);
-    const size_t n_words = eff.size() + (size_t)m + 1;
-    const size_t need = align_up(n_words * sizeof(int32_t), 256) + 256;
-    if (!ws || ws_bytes < need)
-      return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                  ws ? ws_bytes : (size_t)0, need);
-    StagedUpload stage;
-    hipError_t e = stage.begin(n_words * sizeof(int32_t));
-    if (e != hipSuccess) return device_fail(e, "pinned staging buffer");
-    int32_t* h = (int32_t*)stage.host();
-    std::memcpy(h, eff.data(), eff.size() * sizeof(int32_t));
-    int32_t* cum = h + eff.size();
-    int64_t total = 0;
-    cum[0] = 0;
-    for (int32_t i = 0; i < m; ++i) {
-      total += eff[3 * i + 2];
-      cum[i + 1] = (int32_t)total;  // total <= pool rows < 2^31
-    }
-    e = stage.commit(ws, n_words * sizeof(int32_t), st);
-    if (e != hipSuccess) return device_fail(e, "uploading the moves");
-    const int32_t* d_moves = (const int32_t*)ws;
-    const int32_t* d_cum = d_moves + eff.size();
-    for (const pkv::PoolGeom g : {pkv::PoolGeom{(unsigned char*)k_pool, seg_bytes_k, n_kv_heads, block_size},
-                                  pkv::PoolGeom{(unsigned char*)v_pool, seg_bytes_v, n_kv_heads, block_size}}) {
-      if (!g.base) continue;
-      e = pkv::launch_copy_runs(g, d_moves, d_cum, m, (int32_t)total, st);
-      if (e != hipSuccess) return device_fail(e, "copy_cells run launch");
-    }
-    return ok();
-  }
-  // Final source of every row of [lo, hi) after the ordered memmoves.
-  static thread_local std::vector<int32_t> prov, stage_of;
-  static thread_local std::vector<char> changed;
-  prov.resize(hi - lo);
-  for (int64_t r = lo; r < hi; ++r) prov[r - lo] = (int32_t)r;
-  for (int32_t i : order) {
-    const int64_t s = moves[3 * i], d = moves[3 * i + 1], len = moves[3 * i + 2];
-    std::memmove(&prov[d - lo], &prov[s - lo], (size_t)len * sizeof(int32_t));
-  }
-  changed.assign(hi - lo, 0);
-  int64_t n_changed = 0;
-  for (int64_t r = lo; r < hi; ++r)
-    if (prov[r - lo] != r) {
-      changed[r - lo] = 1;
-      ++n_changed;
-    }
-  // Rows read from a row that is also written go through the stage.  The
-  // plan goes straight into the pinned upload buffer: gather pairs (source
-  // row, stage slot) from the start, scatter pairs (row, source row or
-  // -(stage slot + 1)) from word 2 * n_changed on (gather pairs never
-  // outnumber changed rows).
-  const int64_t row_k = seg_bytes_k * n_kv_heads, row_v = v_pool ? seg_bytes_v * n_kv_heads : 0;
-  const size_t n_words = 4 * (size_t)n_changed;
-  const size_t idx_bytes = align_up(n_words * sizeof(int32_t), 256);
-  if (!ws || ws_bytes < idx_bytes)
-    return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                ws ? ws_bytes : (size_t)0, idx_bytes);
-  StagedUpload upl;
-  hipError_t e = upl.begin(n_words * sizeof(int32_t));
-  if (e != hipSuccess) return device_fail(e, "pinned staging buffer");
-  int32_t* gather = (int32_t*)upl.host();
-  int32_t* scatter = gather + 2 * n_changed;
-  stage_of.assign(hi - lo, -1);
-  int32_t n_stage = 0, n_scatter = 0;
-  for (int64_t r = lo; r < hi; ++r) {
-    if (!changed[r - lo]) continue;
-    const int32_t src = prov[r - lo];
-    int32_t y = src;
-    if (changed[src - lo]) {
-      if (stage_of[src - lo] < 0) {
-        gather[2 * n_stage] = src;
-        gather[2 * n_stage + 1] = n_stage;
-        stage_of[src - lo] = n_stage++;
-      }
-      y = -(stage_of[src - lo] + 1);
-    }
-    scatter[2 * n_scatter] = (int32_t)r;
-    scatter[2 * n_scatter + 1] = y;
-    ++n_scatter;
-  }
-  const size_t stage_k = align_up((size_t)n_stage * (size_t)row_k, 256);
-  const size_t stage_v = align_up((size_t)n_stage * (size_t)row_v, 256);
-  const size_t need = idx_bytes + stage_k + stage_v;
-  if (ws_bytes < need) {
-    (void)upl.commit(nullptr, 0, st);
-    return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
-  }
-  int32_t* d_idx = (int32_t*)ws;
-  unsigned char* stage = (unsigned char*)ws + idx_bytes;
-  e = upl.commit(d_idx, n_words * sizeof(int32_t), st);
-  if (e != hipSuccess) return device_fail(e, "uploading the move plan");
-  const int32_t n_gather = n_stage;
-  const int32_t* d_gather = d_idx;
-  const int32_t* d_scatter = d_idx + 2 * n_changed;
-  struct Pool { pkv::PoolGeom g; unsigned char* stage; } pools[2] = {
-      {{(unsigned char*)k_pool, seg_bytes_k, n_kv_heads, block_size}, stage},
-      {{(unsigned char*)v_pool, seg_bytes_v, n_kv_heads, block_size}, stage + stage_k}};
-  for (const Pool& pl : pools) {
-    if (!pl.g.base) continue;
-    e = pkv::launch_copy_rows(1, pl.g, pl.stage, d_gather, n_gather, st);
-    if (e != hipSuccess) return device_fail(e, "copy_cells gather launch");
-  }
-  for (const Pool& pl : pools) {
-    if (!pl.g.base) continue;
-    e = pkv::launch_copy_rows(2, pl.g, pl.stage, d_scatter, n_scatter, st);
-    if (e != hipSuccess) return device_fail(e, "copy_cells scatter launch");
-  }
-  return ok();
 }
 
 pkv_status pkv_resolve_rows(const pkv_shape* sh, int32_t n_q_total, const int32_t* cu_q,

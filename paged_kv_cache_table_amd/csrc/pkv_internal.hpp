@@ -226,12 +226,17 @@ hipError_t launch_prefill(const AttnArgs& a, int combo, int hd, int bs, int g, h
 // Resolver export.
 hipError_t launch_resolve(const AttnArgs& a, int bs, int n_cand, int32_t* rows_out, hipStream_t st);
 // Row copies for copy_cells: a row (token cell) is n_kv_heads segments of
-// seg_bytes, one per kv head, block_size * seg_bytes apart.
+// seg_bytes, one per kv head, block_size * seg_bytes apart.  Rows outside
+// [0, n_rows) (and stage slots outside [0, n_stage)) in a device plan are
+// skipped.
 struct PoolGeom {
   unsigned char* base;
-  int64_t seg_bytes, n_kv_heads, block_size;
+  int64_t seg_bytes, n_kv_heads, block_size, n_rows;
 };
-hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stage,
+// Phase 1: stage[slot] <- pool[row] for pairs (row, slot); phase 2:
+// pool[row] <- pool[src] (src >= 0) or stage[-(src + 1)] for pairs (row,
+// src).  Grid ceil(n_pairs / 4) x 256 threads (one wave per pair).
+hipError_t launch_copy_rows(int phase, const PoolGeom& pool, unsigned char* stage, int32_t n_stage,
                             const int32_t* pairs, int32_t n_pairs, hipStream_t st);
 // Disjoint row moves (no destination touches a source): moves [n][3] and
 // cum [n + 1] (prefix sums of the lengths) on the device; grid

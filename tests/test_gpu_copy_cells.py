@@ -181,9 +181,9 @@ def test_disjoint_moves_bit_exact(seed):
 
 def test_back_to_back_calls_without_synchronizing():
     """Five move sets applied by five calls with no synchronize in between
-    (overlapping and disjoint sets, so both device paths run): the plan
-    uploads take turns on two pinned buffers and each call waits only for
-    the upload out of its own buffer, so a buffer refilled too early would
+    (overlapping and disjoint sets, so both device paths run): each plan is
+    uploaded asynchronously from pinned memory that torch's host allocator
+    keeps until its copy has run, so a plan buffer reused too early would
     show here.  Bit-exact against the oracle applying the sets in turn."""
     import torch
 
@@ -211,8 +211,8 @@ def test_back_to_back_calls_without_synchronizing():
 
 def test_concurrent_calls_from_two_threads():
     """Two host threads apply their own move sets to their own pools at the
-    same time (each on its own stream); the staging buffers are shared and
-    taken in turn.  Each pool bit-exact against the oracle."""
+    same time (each on its own stream); the host plan holds no state, so the
+    threads share nothing.  Each pool bit-exact against the oracle."""
     import threading
 
     import torch
@@ -251,3 +251,75 @@ def test_concurrent_calls_from_two_threads():
         assert job["err"] is None, job["err"]
         assert np.array_equal(job["k"].cpu().numpy(), job["ref"][0])
         assert np.array_equal(job["v"].cpu().numpy(), job["ref"][1])
+
+
+@pytest.mark.parametrize("kind", ["staged rows", "disjoint runs"])
+def test_apply_captured_in_a_graph(kind):
+    """pkv_copy_cells_apply launches kernels only, so it is captured into a
+    HIP graph once (plan made and uploaded before the capture) and every
+    replay moves the rows again: after replay i the pools equal the oracle
+    applying the moves i times.  Eager work and synchronizations run
+    between the replays."""
+    import torch
+
+    rng = np.random.default_rng(95 if kind == "staged rows" else 96)
+    blocks, bs = 96, 16
+    n_rows = blocks * bs
+    kh = _rand_pool(rng, blocks, 4, bs, 256, "u8")
+    vh = _rand_pool(rng, blocks, 4, bs, 128, "float16")
+    if kind == "staged rows":
+        mv = wgen.make_moves(seed=97, n_moves=300, n_rows=n_rows, region=n_rows // 2, max_len=16).moves
+    else:
+        mv = _disjoint_moves(rng, 50, n_rows, 12)
+    k, v = kh.cuda(), vh.cuda()
+    info, plan_h = pkv.copy_cells_plan(mv, n_rows)
+    assert info.kind == (2 if kind == "staged rows" else 1)
+    plan_d = plan_h[: info.n_words].cuda()
+    stage = torch.empty(max(pkv.copy_cells_stage_bytes(info, k, v), 256), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkv.copy_cells_apply(k, v, info, plan_d, stage)
+    torch.cuda.synchronize()
+    # capturing does not run the kernels: the pools are unchanged
+    assert np.array_equal(k.cpu().numpy(), kh.numpy())
+    ref = [kh.numpy().copy(), vh.numpy().copy()]
+    junk = torch.zeros(1 << 20, device="cuda")
+    for i in range(3):
+        g.replay()
+        junk.add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        oracle.copy_cells(ref, mv)
+        assert np.array_equal(k.cpu().numpy().view(np.uint8), ref[0].view(np.uint8)), f"replay {i}"
+        assert np.array_equal(v.cpu().numpy().view(np.uint8), ref[1].view(np.uint8)), f"replay {i}"
+    log(f"  {kind}: {info.n_words} plan words, three replays bit-exact")
+
+
+def test_one_call_c_entry_point():
+    """pkv_kv_copy_cells (plan, upload and apply in one C call, through
+    ctypes) gives the oracle's bytes for an overlapping and a disjoint set."""
+    import ctypes
+
+    import torch
+
+    rng = np.random.default_rng(98)
+    blocks, bs, hkv = 64, 16, 2
+    n_rows = blocks * bs
+    kh = _rand_pool(rng, blocks, hkv, bs, 136, "u8")
+    vh = _rand_pool(rng, blocks, hkv, bs, 64, "float16")
+    k, v = kh.cuda(), vh.cuda()
+    ref = [kh.numpy().copy(), vh.numpy().copy()]
+    L = pkv.lib()
+    for mv in (wgen.make_moves(seed=99, n_moves=200, n_rows=n_rows, region=n_rows // 2, max_len=16).moves,
+               _disjoint_moves(rng, 30, n_rows, 8)):
+        mv = np.ascontiguousarray(mv.astype(np.int32))
+        oracle.copy_cells(ref, mv)
+        # K segments are 136 bytes, V segments 64 bytes (32 halves)
+        need = L.pkv_copy_cells_workspace_bytes(mv.ctypes.data, mv.shape[0], 136 * hkv, 64 * hkv)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        st = L.pkv_kv_copy_cells(k.data_ptr(), v.data_ptr(), blocks, bs, hkv, 136, 64, mv.ctypes.data,
+                                 mv.shape[0], ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, pkv.last_error()
+    torch.cuda.synchronize()
+    assert np.array_equal(k.cpu().numpy(), ref[0])
+    assert np.array_equal(v.cpu().numpy().view(np.uint8), ref[1].view(np.uint8))

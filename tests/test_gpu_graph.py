@@ -35,7 +35,7 @@ def _capture(fn):
 def test_decode_graph_replays_equal_eager(kind):
     """direct: a small call (one workgroup per possible slot); planned: 64
     sequences x 32 possible 1024-position slots x 8 kv heads, so the call
-    runs the plan kernel (work list, cut slots) inside the graph."""
+    lists its work items (cut slots included) inside the graph."""
     import torch
 
     if kind == "direct":
