@@ -60,7 +60,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 constexpr int kPWaves = 8;          // waves per workgroup (two per SIMD)
-constexpr int kRing = 3;            // LDS tile slots: copies run two tiles ahead
+constexpr int kRing = 4;            // LDS tile slots: copies run three tiles ahead
 constexpr float kEmptyMax = -1e30f;
 constexpr float kLazyMax = 8.0f;    // log2 growth of a row max that forces a rescale
 constexpr int kTargetTasks = 512;   // workgroups the chunking aims for
@@ -643,28 +643,32 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   };
 
   // ---- pipeline: tile k is computed while tile k+1 is being prepared and
-  // tile k+2 copied; one barrier per tile
-  if (ntl > 0) {
-    issue(0, 0);
-    if (ntl > 1) issue(1, 1);
-    if (ntl > 1) wait_vm<NDMA>();
+  // tiles k+2 .. k+kRing-1 are being copied; tile t lives in slot t % kRing;
+  // one barrier per tile
+  constexpr int AH = kRing - 1;  // tiles whose copies run ahead of the computed one
+  // wait until at most n tiles' copies of this wave are still in flight
+  auto wait_tiles = [&](int n) {
+    if (n >= 2) wait_vm<2 * NDMA>();
+    else if (n == 1) wait_vm<NDMA>();
     else wait_vm<0>();
+  };
+  static_assert(AH <= 3, "wait_tiles covers at most two tiles in flight");
+  if (ntl > 0) {
+    for (int i = 0; i < AH && i < ntl; ++i) issue(i, i);
+    wait_tiles((ntl < AH ? ntl : AH) - 1);
     prepare(0, 0, tile_at(0));
     __syncthreads();
-    int sl = 0;
     for (int k = 0;; ++k) {
-      const int sl1 = sl == 2 ? 0 : sl + 1, sl2 = sl1 == 2 ? 0 : sl1 + 1;
-      if (k + 2 < ntl) issue(sl2, k + 2);
-      compute(sl, k & 1, tile_at(k));
+      if (k + AH < ntl) issue((k + AH) % kRing, k + AH);
+      compute(k % kRing, k & 1, tile_at(k));
       // prepare tile k+1 once this wave's copies of it have landed
       if (k + 1 < ntl) {
-        if (k + 2 < ntl) wait_vm<NDMA>();
-        else wait_vm<0>();
-        prepare(sl1, (k + 1) & 1, tile_at(k + 1));
+        const int later = ntl - (k + 2);  // tiles issued after k+1 that may still be in flight
+        wait_tiles(later < AH - 1 ? later : AH - 1);
+        prepare((k + 1) % kRing, (k + 1) & 1, tile_at(k + 1));
       }
       __syncthreads();
       if (k + 1 >= ntl) break;
-      sl = sl1;
     }
   }
   if (bad && (a.flags & PKV_FLAG_CHECKED) && a.err && kvh == 0 && qb == 0 && t == 0) atomicAdd(a.err, bad);

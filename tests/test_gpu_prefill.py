@@ -149,3 +149,21 @@ def test_prefill_more_sequences_than_the_order_sort_holds():
     out, lse = d.decode()
     ro, rl = d.oracle()
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), "4100 seqs decode")
+
+
+def test_prefill_chunk_merge_is_deterministic():
+    """Two long sequences x 8 kv heads: each window is cut into many chunks
+    whose workgroups finish in no fixed order; the last to finish merges the
+    group in chunk order, so repeated calls give the same bits, and match
+    the oracle."""
+    import torch
+
+    w = wgen.make_custom(seed=31, n_seqs=2, n_q_heads=32, n_kv_heads=8, head_dim=128, block_size=32,
+                         fmts=("f16", "q8_0", "f16"), ctx=(3000, 6000), mode="kv_map", n_runs=4, kind="prefill",
+                         q_per_seq=(40, 64), hole_frac=0.02)
+    d = Dev(w)
+    outs = [d.prefill() for _ in range(3)]
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    ro, rl = d.oracle()
+    compare(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), ro, rl, tol_of(w), "many chunks")
