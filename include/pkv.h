@@ -199,9 +199,14 @@ pkv_status pkv_paged_attn_decode_noalloc(const pkv_shape* shape, const void* q, 
 /* ---------------------------------------------------------------------------
  * Windowed prefill: a chunk of queries per sequence against its window,
  * causal inside the window ("KV Cache Design", section 1: the fast windowed
- * prefill families for more than one query).  QK^T and PV run on the matrix
- * cores.  Query j of sequence s sees W_s intersected with
- * [0, min(seq_len_s, q_pos_j + 1)) minus holes.
+ * prefill families for more than one query, in _f32 and _f16 variants).
+ * Query j of sequence s sees W_s intersected with
+ * [0, min(seq_len_s, q_pos_j + 1)) minus holes.  f16 queries (K f16 or
+ * q8_0, V f16): QK^T and PV run on the matrix cores (probabilities rounded
+ * to f16 for PV).  f32 queries (K f32 or q8_0, V f32): every product and
+ * sum stays in f32, computed by the decode kernels with each query as its
+ * own decode sequence (its sequence's table and window, length
+ * min(seq_len_s, q_pos_j + 1)); then n_q_total may be at most 65535.
  *
  * n_q_total: rows of q.  cu_q: int32 [n_seqs + 1], queries of sequence s are
  * rows cu_q[s] .. cu_q[s+1]-1 (non-decreasing, cu_q[0] = 0, cu_q[n_seqs] =

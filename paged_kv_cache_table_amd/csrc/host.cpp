@@ -317,6 +317,42 @@ pkv_status decode_impl(DecodePart part, const pkv_shape* sh, const void* q, cons
   return ok();
 }
 
+// f32 prefill (q f32; K f32 or q8_0; V f32) runs through the decode
+// kernels, one virtual decode sequence per query (prefill_f32.hip): the
+// workspace holds the virtual tables, lengths and windows, a flag per query,
+// the decode output and the decode workspace.
+struct F32Prefill {
+  pkv_shape vsh;
+  Plan VP;
+  int win_ints = 0;
+  size_t off_vtable = 0, off_vlens = 0, off_vwin = 0, off_comp = 0, off_out = 0, off_lse = 0, off_dec = 0,
+         total = 0;
+};
+
+pkv_status plan_f32_prefill(const pkv_shape* sh, int32_t n_q_total, int32_t mode, int32_t n_runs,
+                            F32Prefill* F) {
+  if (n_q_total > 65535)
+    return fail(PKV_E_UNSUPPORTED,
+                "f32 prefill computes each query as a decode sequence: n_q_total %d is above 65535", n_q_total);
+  F->vsh = *sh;
+  F->vsh.n_seqs = n_q_total;
+  F->vsh.split_tokens = 0;
+  static const int32_t dummy[2] = {0, 0};
+  pkv_status st = plan_decode(&F->vsh, mode, n_runs, mode == PKV_WIN_CAUSAL ? nullptr : dummy, &F->VP);
+  if (st) return st;
+  F->win_ints = mode == PKV_WIN_SPAN ? 2 : (mode == PKV_WIN_KV_MAP ? 2 * n_runs : 0);
+  const size_t nq = (size_t)n_q_total;
+  F->off_vtable = 0;
+  F->off_vlens = F->off_vtable + align_up(nq * sh->max_blocks_per_seq * sizeof(int32_t), 256);
+  F->off_vwin = F->off_vlens + align_up(nq * sizeof(int32_t), 256);
+  F->off_comp = F->off_vwin + align_up(nq * F->win_ints * sizeof(int32_t), 256);
+  F->off_out = F->off_comp + align_up(nq, 256);
+  F->off_lse = F->off_out + align_up(nq * sh->n_q_heads * sh->head_dim * sizeof(float), 256);
+  F->off_dec = F->off_lse + align_up(nq * sh->n_q_heads * sizeof(float), 256);
+  F->total = F->off_dec + F->VP.total;
+  return PKV_OK;
+}
+
 }  // namespace
 
 namespace pkv_host {
@@ -380,6 +416,11 @@ size_t pkv_prefill_workspace_bytes(const pkv_shape* shape, int32_t n_q_total,
   static const int32_t dummy[2] = {0, 0};
   if (check_attn(shape, mode, n_runs, mode == PKV_WIN_CAUSAL ? nullptr : dummy, &P)) return 0;
   if (n_q_total < 0 || max_q_per_seq < 0) return 0;
+  if (P.combo == pkv::kComboF32 || P.combo == pkv::kComboQ8F) {
+    F32Prefill F;
+    if (plan_f32_prefill(shape, n_q_total, mode, n_runs, &F)) return 0;
+    return F.total;
+  }
   pkv::AttnArgs a = base_args(shape, P);
   a.mode = mode;
   a.n_q_total = n_q_total;
@@ -420,6 +461,31 @@ pkv_status pkv_paged_attn_prefill_window(const pkv_shape* sh, int32_t n_q_total,
   a.lse = lse;
   a.n_q_total = n_q_total;
   a.max_q = max_q_per_seq;
+  if (P.combo == pkv::kComboF32 || P.combo == pkv::kComboQ8F) {
+    F32Prefill F;
+    st = plan_f32_prefill(sh, n_q_total, mode, n_runs, &F);
+    if (st) return st;
+    if (!ws || ws_bytes < F.total)
+      return fail(PKV_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  ws ? ws_bytes : (size_t)0, F.total);
+    if (((uintptr_t)ws) % 256) return fail(PKV_E_WORKSPACE, "workspace must be 256-byte aligned");
+    char* w = (char*)ws;
+    int32_t* vtable = (int32_t*)(w + F.off_vtable);
+    int32_t* vlens = (int32_t*)(w + F.off_vlens);
+    int32_t* vwin = F.win_ints ? (int32_t*)(w + F.off_vwin) : nullptr;
+    uint8_t* comp = (uint8_t*)(w + F.off_comp);
+    float* tmp_out = (float*)(w + F.off_out);
+    float* tmp_lse = (float*)(w + F.off_lse);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = pkv::launch_prefill_expand(a, vtable, vlens, vwin, F.win_ints, comp, s);
+    if (e != hipSuccess) return device_fail(e, "prefill expand launch");
+    st = decode_impl(kBoth, &F.vsh, q, k_pool, v_pool, vtable, vlens, mode, n_runs, vwin, tmp_out, tmp_lse,
+                     w + F.off_dec, F.VP.total, stream);
+    if (st) return st;
+    e = pkv::launch_prefill_copy_rows(tmp_out, tmp_lse, comp, out, lse, n_q_total, sh->n_q_heads, sh->head_dim, s);
+    if (e != hipSuccess) return device_fail(e, "prefill copy launch");
+    return ok();
+  }
   bool found = false;
   const size_t need = pkv::prefill_workspace(a, P.combo, sh->head_dim, sh->block_size, P.g, &found);
   if (!found)

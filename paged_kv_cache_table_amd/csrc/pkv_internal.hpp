@@ -223,6 +223,14 @@ hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st);
 size_t prefill_workspace(const AttnArgs& a, int combo, int hd, int bs, int g, bool* found);
 hipError_t launch_prefill(const AttnArgs& a, int combo, int hd, int bs, int g, hipStream_t st,
                           bool* found);
+// f32 prefill through the decode kernels (prefill_f32.hip): per query its
+// virtual table row, length and window, whether prefill computes it; then
+// the computed rows of the decode output copied out.
+hipError_t launch_prefill_expand(const AttnArgs& a, int32_t* vtable, int32_t* vlens, int32_t* vwin,
+                                 int32_t win_ints, uint8_t* computed, hipStream_t st);
+hipError_t launch_prefill_copy_rows(const float* tmp_out, const float* tmp_lse, const uint8_t* computed,
+                                    float* out, float* lse, int64_t n_rows, int32_t hq, int32_t hd,
+                                    hipStream_t st);
 // Resolver export.
 hipError_t launch_resolve(const AttnArgs& a, int bs, int n_cand, int32_t* rows_out, hipStream_t st);
 // Row copies for copy_cells: a row (token cell) is n_kv_heads segments of

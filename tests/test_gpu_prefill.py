@@ -90,18 +90,55 @@ def test_prefill_rows_past_max_q_are_untouched():
         assert np.all(o[a + 10 : b] == 7.0) and np.all(l[a + 10 : b] == 7.0)
 
 
-def test_prefill_refuses_f32_and_leaves_outputs():
+@pytest.mark.parametrize("hd,bs", [(64, 16), (128, 16), (256, 16), (128, 32)])
+@pytest.mark.parametrize("kfmt", ["f32", "q8_0"])
+@pytest.mark.parametrize("g", [1, 4, 8])
+def test_prefill_f32_formats(hd, bs, kfmt, g):
+    """f32 queries with f32 or q8_0 K and f32 V: every product and sum in
+    f32, held to 1e-5 against the oracle."""
+    w = wgen.make_custom(seed=hd + bs + 7 * g + (kfmt == "q8_0"), n_seqs=4, n_q_heads=2 * g, n_kv_heads=2,
+                         head_dim=hd, block_size=bs, fmts=("f32", kfmt, "f32"), ctx=(1, 300), kind="prefill",
+                         q_per_seq=(1, 40), mode="causal", hole_frac=0.05)
+    log(f"f32 prefill hd {hd} bs {bs} g {g} K {kfmt}")
+    d, out, lse, ro, rl = _run(w)
+    compare(out, lse, ro, rl, 1e-5, f"f32 hd{hd} bs{bs} g{g} {kfmt}")
+
+
+@pytest.mark.parametrize("mode", ["span", "kv_map"])
+@pytest.mark.parametrize("kfmt", ["f32", "q8_0"])
+def test_prefill_f32_windows_and_degenerate(mode, kfmt):
+    w = wgen.make_custom(seed=55, n_seqs=6, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=32,
+                         fmts=("f32", kfmt, "f32"), ctx=(1, 500), mode=mode, n_runs=5, kind="prefill",
+                         q_per_seq=(1, 50), hole_frac=0.1)
+    if mode == "span":
+        w.window[0] = (5, 5)  # empty window
+    else:
+        w.kv_map[0] = 0       # no runs
+    w.block_table[1, :] = -1  # all holes
+    d, out, lse, ro, rl = _run(w)
+    for s in (0, 1):
+        rows = slice(w.cu_q[s], w.cu_q[s + 1])
+        assert np.all(out[rows] == 0) and np.all(np.isneginf(lse[rows]))
+    compare(out, lse, ro, rl, 1e-5, f"f32 {mode} {kfmt}")
+
+
+def test_prefill_f32_rows_past_max_q_are_untouched():
     import torch
 
-    w = wgen.make_custom(seed=23, n_seqs=2, n_q_heads=4, n_kv_heads=2, head_dim=64, block_size=16,
-                         fmts=("f32", "f32", "f32"), ctx=(10, 40), kind="prefill")
+    w = wgen.make_custom(seed=56, n_seqs=3, n_q_heads=8, n_kv_heads=2, head_dim=64, block_size=16,
+                         fmts=("f32", "f32", "f32"), ctx=(60, 120), kind="prefill", q_per_seq=(20, 30),
+                         hole_frac=0.0)
     d = Dev(w)
-    out = torch.full((w.n_queries, 4, 64), 7.0, device="cuda")
-    with pytest.raises(pkv.PkvError) as ei:
-        d.prefill(out=out)
-    assert ei.value.status == 2 and "prefill" in ei.value.message
-    torch.cuda.synchronize()
-    assert torch.all(out == 7.0)
+    out = torch.full((w.n_queries, 8, 64), 7.0, device="cuda")
+    lse = torch.full((w.n_queries, 8), 7.0, device="cuda")
+    pkv.paged_attn_prefill_window(d.q, d.cu_q, d.q_pos, d.k, d.v, d.table, d.lens, w.scale, 10,
+                                  mode="causal", out=out, lse=lse)
+    ro, rl = d.oracle()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for s in range(w.n_seqs):
+        a, b = int(w.cu_q[s]), int(w.cu_q[s + 1])
+        compare(o[a : a + 10], l[a : a + 10], ro[a : a + 10], rl[a : a + 10], 1e-5, f"f32 seq {s} first 10")
+        assert np.all(o[a + 10 : b] == 7.0) and np.all(l[a + 10 : b] == 7.0)
 
 
 def test_prefill_matches_decode_for_last_queries():
