@@ -147,7 +147,7 @@ pkv_status check_attn(const pkv_shape* sh, int mode, int n_runs, const void* win
 // the tail.  Depends on the shape only.
 int auto_split(const pkv_shape* sh, int runs) {
   const int64_t ctx = (int64_t)sh->max_blocks_per_seq * sh->block_size;
-  const int64_t target = 3072;
+  const int64_t target = 6144;
   for (int nb : {64, 32, 16, 8}) {
     const int64_t sp = (int64_t)nb * sh->block_size;
     const int64_t items = (int64_t)sh->n_seqs * sh->n_kv_heads * runs * ((ctx + sp - 1) / sp);

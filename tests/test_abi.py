@@ -130,7 +130,8 @@ def test_window_and_workspace_refusals():
 def test_decode_workspace_size_formula():
     sh = _shape(n_seqs=64, n_q_heads=32, n_kv_heads=8, max_blocks_per_seq=2048, split_tokens=512)
     assert pkv.decode_split_tokens(_shape(n_seqs=64, n_q_heads=32, n_kv_heads=8, max_blocks_per_seq=2048)) == 1024
-    assert pkv.decode_split_tokens(_shape(n_seqs=32, n_q_heads=9, n_kv_heads=3, head_dim=64, max_blocks_per_seq=512)) == 256
+    # the largest split that still gives >= 6144 possible items: 32 x 3 x 8192 / 128
+    assert pkv.decode_split_tokens(_shape(n_seqs=32, n_q_heads=9, n_kv_heads=3, head_dim=64, max_blocks_per_seq=512)) == 128
     def up(x):
         return (x + 255) // 256 * 256
 
