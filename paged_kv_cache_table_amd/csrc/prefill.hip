@@ -64,7 +64,7 @@ constexpr int kPWaves = 8;          // waves per workgroup (two per SIMD)
 constexpr int kRing = 4;            // LDS tile slots: copies run three tiles ahead
 constexpr float kEmptyMax = -1e30f;
 constexpr float kLazyMax = 8.0f;    // log2 growth of a row max that forces a rescale
-constexpr int kTargetTasks = 512;   // workgroups the chunking aims for
+constexpr int kTargetTasks = 384;   // workgroups the chunking aims for (1.5 per CU)
 constexpr int kMaxChunks = 16;      // unless a chunk would exceed kMaxTiles
 constexpr int kMaxTiles = 256;      // tiles of one workgroup's chunk (its list lives in LDS)
 
@@ -114,7 +114,7 @@ struct __attribute__((aligned(16))) PrefillSmem {
   float ksc[KQ8 ? 2 : 1][KQ8 ? Gm::KS : 1][KQ8 ? Gm::T : 4];
   unsigned char raw[KQ8 ? kRing : 1][KQ8 ? kPWaves * Gm::RAWW : 16];  // q8_0 tiles as stored
   TileRec tiles[kMaxTiles];                                           // this workgroup's chunk
-  int32_t lim_max;                                                    // largest causal limit of the rows
+  int32_t lim_max[kPWaves];                                           // each wave's largest causal limit
 };
 
 // Row r's 16-byte chunks are stored XOR-permuted by a key of the row so that
@@ -197,13 +197,15 @@ __device__ __forceinline__ void codes_to_f16(uint32_t x, half2_t& lo, half2_t& h
   hi = __builtin_bit_cast(half2_t, phi) - bias;
 }
 
-// Run r of sequence s clipped to [0, limit) (same rule as run_range; reads
-// the window through a pointer the compiler may load with scalar loads).
-__device__ inline void run_bounds(const AttnArgs& a, const int32_t* __restrict__ window, int s, int r,
-                                  int32_t limit, int32_t& lo, int32_t& hi) {
-  int64_t x0 = 0, x1 = 0;
+// Run r of sequence s as stored, [x0, x1) before clipping (same rule as
+// run_range; reads the window through a pointer the compiler may load with
+// scalar loads).  Causal mode has one run, [0, any limit).
+__device__ inline void raw_run(const AttnArgs& a, const int32_t* __restrict__ window, int s, int r, int64_t& x0,
+                               int64_t& x1) {
+  x0 = 0;
+  x1 = 0;
   if (a.mode == PKV_WIN_CAUSAL) {
-    x1 = limit;
+    x1 = INT64_MAX;
   } else if (a.mode == PKV_WIN_SPAN) {
     x0 = window[2 * s];
     x1 = window[2 * s + 1];
@@ -215,28 +217,12 @@ __device__ inline void run_bounds(const AttnArgs& a, const int32_t* __restrict__
       x1 = c + n;
     }
   }
-  if (x0 < 0) x0 = 0;
-  if (x1 > limit) x1 = limit;
-  if (x1 < x0) x1 = x0;
-  lo = uni((int32_t)x0);
-  hi = uni((int32_t)x1);
 }
 
 // The runs of a sequence's window, clipped to [0, lim), each covered by the
 // T-aligned tiles that meet it (its first and last tile may be partial); the
 // runs' tiles in order form one list that is cut into the chunks.
-template <int T>
-struct WalkCtx {
-  const AttnArgs& a;
-  const int32_t* __restrict__ window;
-  int s;
-  int32_t lim;
-
-  __device__ int32_t tiles(int r, int32_t& lo, int32_t& hi) const {
-    run_bounds(a, window, s, r, lim, lo, hi);
-    return hi > lo ? (hi + T - 1) / T - lo / T : 0;
-  }
-};
+constexpr int kPreRuns = 4;  // runs a workgroup keeps in registers
 
 // One staged tile (wave-uniform): it starts at t0 (a multiple of T) and vm
 // has bit p set when position t0 + p is visible (inside the run, not in a
@@ -287,15 +273,79 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   if (j0 >= q1) return;  // whole workgroup: no queries here
   const int j1 = j0 + QPB < q1 ? j0 + QPB : q1;
   const int32_t L = clamp_seq_len(a.seq_lens[s], a.max_blocks, BS);
+  // the window's first runs, loaded beside cu_q and seq_lens (wave-uniform)
+  int64_t px0[kPreRuns], px1[kPreRuns];
+#pragma unroll
+  for (int r = 0; r < kPreRuns; ++r) {
+    px0[r] = 0;
+    px1[r] = 0;
+    if (r < a.n_runs) raw_run(a, window, s, r, px0[r], px1[r]);
+  }
+  // run r clipped to [0, limit), and the number of tiles that cover it
+  auto run_tiles = [&](int r, int32_t limit, int32_t& lo, int32_t& hi) {
+    int64_t x0 = px0[0], x1 = px1[0];
+#pragma unroll
+    for (int i = 1; i < kPreRuns; ++i)
+      if (r == i) {
+        x0 = px0[i];
+        x1 = px1[i];
+      }
+    if (r >= kPreRuns) raw_run(a, window, s, r, x0, x1);
+    if (x0 < 0) x0 = 0;
+    if (x1 > limit) x1 = limit;
+    if (x1 < x0) x1 = x0;
+    lo = uni((int32_t)x0);
+    hi = uni((int32_t)x1);
+    return hi > lo ? (hi + T - 1) / T - lo / T : 0;
+  };
+  // tile idx of the list clipped to [0, limit): its start and its run
+  auto tile_at_list = [&](int32_t idx, int32_t limit, int32_t& t0, int32_t& lo, int32_t& hi) {
+    lo = 0;
+    hi = 0;
+    for (int r = 0; r < a.n_runs; ++r) {
+      const int32_t n = run_tiles(r, limit, lo, hi);
+      if (idx < n) break;
+      idx -= n;
+    }
+    t0 = (lo / T + idx) * T;
+  };
+  // this chunk of the list clipped to [0, limit): first tile and count
+  auto chunk_of = [&](int32_t limit, int32_t& NT, int32_t& ta, int32_t& ntl) {
+    NT = 0;
+    for (int r = 0; r < a.n_runs; ++r) {
+      int32_t lo, hi;
+      NT += run_tiles(r, limit, lo, hi);
+    }
+    const int32_t per = (NT + a.nch - 1) / a.nch;
+    ta = c * per;
+    ntl = (ta + per < NT ? ta + per : NT) - ta;
+    if (ntl > kMaxTiles) ntl = kMaxTiles;  // the host sizes chunks below this
+    if (ntl < 0) ntl = 0;
+  };
+  const int32_t* trow = table + (int64_t)s * a.max_blocks;
 
   // ---- rows of this lane: row tile rt covers rows (w * RT + rt) * 16 + n16
   int jq[RT], hq[RT];
   bool rok[RT];
   int32_t lim[RT];
   half8_t qf[RT][KS];
-  if (t == 0) sm.lim_max = 0;
-  __syncthreads();
-  int32_t lmin = 0x7fffffff;
+  // The table entries of this chunk's tiles, loaded beside the queries'
+  // positions: the chunk is cut from the list clipped to the sequence
+  // length, and the entries are used if the queries' causal limit leaves
+  // that tile where it was (always when the queries end the sequence).
+  int32_t NTs, tas, ntls, t0s = -1;
+  chunk_of(L, NTs, tas, ntls);
+  int32_t spec[4] = {-1, -1, -1, -1};
+  if (t < ntls) {
+    int32_t lo, hi;
+    tile_at_list(tas + t, L, t0s, lo, hi);
+#pragma unroll
+    for (int j = 0; j < NID; ++j) {
+      const int32_t b = t0s / BS + j;
+      spec[j] = b < a.max_blocks ? trow[b] : -1;
+    }
+  }
+  int32_t lmin = 0x7fffffff, lmax = 0;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int rr = (w * RT + rt) * 16 + n16;
@@ -318,46 +368,40 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       if (rok[rt]) v = *(const half8_t*)(qrow + ks * 32 + g * 8);
       qf[rt][ks] = a.score_mul < 0.f ? -v : v;  // a negative scale: negate q (exact), use |scale|
     }
-    if (rok[rt]) atomicMax(&sm.lim_max, lim[rt]);
+    if (rok[rt] && lim[rt] > lmax) lmax = lim[rt];
   }
-  // smallest causal limit over the wave's rows (wave-uniform)
+  // smallest and largest causal limit over the wave's rows (wave-uniform);
+  // the largest over the workgroup bounds its tile list
 #pragma unroll
   for (int mm = 1; mm < 64; mm <<= 1) {
     const int32_t o = __shfl_xor(lmin, mm, 64);
     lmin = o < lmin ? o : lmin;
+    const int32_t x = __shfl_xor(lmax, mm, 64);
+    lmax = x > lmax ? x : lmax;
   }
   const int32_t lim_min_w = uni(lmin);
+  if (l == 0) sm.lim_max[w] = lmax;
   __syncthreads();
-  const int32_t lim_max = uni(sm.lim_max);
+  int32_t lim_max = 0;
+#pragma unroll
+  for (int i = 0; i < kPWaves; ++i) lim_max = sm.lim_max[i] > lim_max ? sm.lim_max[i] : lim_max;
+  lim_max = uni(lim_max);
 
   // ---- this workgroup's chunk of the window's tile list
-  const WalkCtx<T> wx{a, window, s, lim_max};
-  int32_t NT = 0;
-  for (int r = 0; r < a.n_runs; ++r) {
-    int32_t lo, hi;
-    NT += wx.tiles(r, lo, hi);
-  }
-  const int32_t per = (NT + a.nch - 1) / a.nch;
-  const int32_t ta = c * per;
-  int32_t ntl = (ta + per < NT ? ta + per : NT) - ta;  // tiles in this chunk
-  if (ntl > kMaxTiles) ntl = kMaxTiles;                // the host sizes chunks below this
-  if (ntl < 0) ntl = 0;
+  int32_t NT, ta, ntl;
+  chunk_of(lim_max, NT, ta, ntl);
 
   const unsigned char* kbase = kpool + (int64_t)kvh * BS * a.k_seg_bytes;
   const unsigned char* vbase = vpool + (int64_t)kvh * BS * a.v_seg_bytes;
-  const int32_t* trow = table + (int64_t)s * a.max_blocks;
   int32_t bad = 0;  // out-of-range table entries seen (checked mode)
 
-  // thread i describes tile ta + i of the list
-  for (int i = t; i < ntl; i += 64 * kPWaves) {
-    int32_t idx = ta + i, lo = 0, hi = 0;
-    for (int r = 0; r < a.n_runs; ++r) {
-      const int32_t n = wx.tiles(r, lo, hi);
-      if (idx < n) break;
-      idx -= n;
-    }
+  // thread i describes tile ta + i of the list (ntl <= kMaxTiles < 512)
+  static_assert(kMaxTiles <= 64 * kPWaves, "one tile per thread");
+  if (t < ntl) {
+    int32_t lo, hi;
     TileRec rc;
-    rc.t0 = (lo / T + idx) * T;
+    tile_at_list(ta + t, lim_max, rc.t0, lo, hi);
+    const bool reuse = NT == NTs && ta == tas && rc.t0 == t0s;
     const int32_t vlo = (lo > rc.t0 ? lo : rc.t0) - rc.t0;
     const int32_t vhi = (hi < rc.t0 + T ? hi : rc.t0 + T) - rc.t0;
     uint64_t vm = (vhi >= 64 ? ~0ull : (1ull << vhi) - 1ull) & ~((1ull << vlo) - 1ull);
@@ -367,7 +411,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       int32_t id = -1;
       if (j < NID) {
         const int32_t b = rc.t0 / BS + j;
-        const int32_t raw = b < a.max_blocks ? trow[b] : -1;
+        const int32_t raw = reuse ? spec[j] : (b < a.max_blocks ? trow[b] : -1);
         const bool ok = raw >= 0 && raw < a.n_pool_blocks;
         const uint64_t bm = ((1ull << BS) - 1ull) << (j * BS);
         if (!ok && raw != -1 && (vm & bm)) ++bad;
@@ -378,7 +422,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     }
     rc.vm_lo = (uint32_t)vm;
     rc.vm_hi = (uint32_t)(vm >> 32);
-    sm.tiles[i] = rc;
+    sm.tiles[t] = rc;
   }
   __syncthreads();
 
@@ -621,7 +665,10 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       // ---- O^T += V^T P^T: two transposing reads give lane (g, n16) column
       // dt*16 + n16 of V at positions 16 h + 4 g + e of the half (operand
       // element 4 h + e); lane n16 addresses row 16 h + 4 g + n16 / 4 of the
-      // half at columns dt*16 + 4 (n16 % 4) ...
+      // half at columns dt*16 + 4 (n16 % 4) ...  The wave raises its priority
+      // for these matrix instructions, so the two waves of a SIMD drift apart
+      // and one's vector work overlaps the other's matrix work.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         half8_t vf;
@@ -643,6 +690,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       // row sums of the rounded probabilities (every element of o[rt][DT])
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) o[rt][DT] = mfma16x16x32(ones, pf[rt], o[rt][DT]);
+      __builtin_amdgcn_s_setprio(0);
       // Issue order of this block (a scheduling hint; no effect on values):
       // the K fragment reads run four ahead of the matrix instructions that
       // use them, three vector instructions (the exponentials) sit between
@@ -828,7 +876,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a) {
 
 namespace {
 
-// Chunks per window: enough workgroups to fill the chip twice over, each
+// Chunks per window: about one and a half workgroups per CU (one fits a CU at a time;
+// the longest chunks go first and the short ones fill in behind them), each
 // chunk still at least four tiles of the largest possible window, and never
 // more than kMaxTiles tiles (a run of the table's width spans at most
 // width / T + 2 tiles).
