@@ -115,8 +115,6 @@ struct __attribute__((aligned(16))) PrefillSmem {
   unsigned char raw[KQ8 ? kRing : 1][KQ8 ? kPWaves * Gm::RAWW : 16];  // q8_0 tiles as stored
   TileRec tiles[kMaxTiles];                                           // this workgroup's chunk
   int32_t lim_max[kPWaves];                                           // each wave's largest causal limit
-  uint64_t okey[kInlineOrderMax];                                     // sequence order keys
-  int32_t sel;                                                        // this workgroup's sequence
 };
 
 // Row r's 16-byte chunks are stored XOR-permuted by a key of the row so that
@@ -226,26 +224,6 @@ __device__ inline void raw_run(const AttnArgs& a, const int32_t* __restrict__ wi
 // runs' tiles in order form one list that is cut into the chunks.
 constexpr int kPreRuns = 4;  // runs a workgroup keeps in registers
 
-// Sort key of sequence i for the longest-first order: its window clipped to
-// the sequence length, in T-aligned tiles (about the prefill work per
-// sequence; the queries' causal limits are not consulted), descending, ties
-// by index.
-template <int T, int BS>
-__device__ inline uint64_t order_key(const AttnArgs& a, int i) {
-  const int32_t L = clamp_seq_len(a.seq_lens[i], a.max_blocks, BS);
-  int32_t nt = 0;
-  for (int r = 0; r < a.n_runs; ++r) {
-    int32_t lo, hi;
-    run_range(a, i, r, L, lo, hi);
-    nt += hi > lo ? (hi + T - 1) / T - lo / T : 0;
-  }
-  return ((uint64_t)(uint32_t)(0x7fffffff - nt) << 32) | (uint32_t)i;
-}
-
-// Up to this many sequences each workgroup ranks them itself; above it a
-// separate kernel sorts them once.
-constexpr int kInlineOrderMax = 64;
-
 // One staged tile (wave-uniform): it starts at t0 (a multiple of T) and vm
 // has bit p set when position t0 + p is visible (inside the run, not in a
 // hole).
@@ -283,25 +261,10 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   rest /= a.n_kv_heads;
   const int c = rest % a.nch;
   const int32_t rank = rest / a.nch;
-  const int t = threadIdx.x, w = uni(t >> 6), l = t & 63, g = l >> 4, n16 = l & 15;
-  int s;
-  if (a.n_seqs <= kInlineOrderMax) {
-    // the sequence of rank `rank` in the longest-first order
-    if (t < a.n_seqs) sm.okey[t] = order_key<T, BS>(a, t);
-    __syncthreads();
-    if (t < a.n_seqs) {
-      const uint64_t key = sm.okey[t];
-      int32_t r = 0;
-      for (int j = 0; j < a.n_seqs; ++j) r += sm.okey[j] < key ? 1 : 0;
-      if (r == rank) sm.sel = t;
-    }
-    __syncthreads();
-    s = uni(sm.sel);
-  } else {
-    s = order[rank];
-  }
+  int s = order[rank];
   s = s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
 
+  const int t = threadIdx.x, w = uni(t >> 6), l = t & 63, g = l >> 4, n16 = l & 15;
   int q0 = a.cu_q[s], q1 = a.cu_q[s + 1];
   q0 = q0 < 0 ? 0 : (q0 > a.n_q_total ? a.n_q_total : q0);
   q1 = q1 < q0 ? q0 : (q1 > a.n_q_total ? a.n_q_total : q1);
@@ -815,10 +778,9 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   }
 }
 
-// Orders the sequences by order_key (decreasing number of window tiles,
-// ties by index) for batches above kInlineOrderMax sequences; one
-// workgroup, bitonic sort in LDS.  More than kOrderMax sequences keep their
-// own order.
+// Orders the sequences by decreasing number of window tiles (about the
+// prefill kernel's work per sequence), ties by index; one workgroup, bitonic
+// sort in LDS.  More than kOrderMax sequences keep their own order.
 constexpr int kOrderMax = 4096;
 
 template <int T, int BS>
@@ -831,7 +793,22 @@ __global__ __launch_bounds__(1024) void prefill_order_kernel(AttnArgs a, int32_t
   }
   int np = 1;
   while (np < n) np <<= 1;
-  for (int i = t; i < np; i += 1024) key[i] = i < n ? order_key<T, BS>(a, i) : ~0ull;  // padding sorts last
+  for (int i = t; i < np; i += 1024) {
+    uint64_t kk = ~0ull;  // padding sorts last
+    if (i < n) {
+      // the window clipped to the sequence length (the order only needs to
+      // be roughly right, so the queries' causal limits are not consulted)
+      const int32_t L = clamp_seq_len(a.seq_lens[i], a.max_blocks, BS);
+      int32_t nt = 0;
+      for (int r = 0; r < a.n_runs; ++r) {
+        int32_t lo, hi;
+        run_range(a, i, r, L, lo, hi);
+        nt += hi > lo ? (hi + T - 1) / T - lo / T : 0;
+      }
+      kk = ((uint64_t)(uint32_t)(0x7fffffff - nt) << 32) | (uint32_t)i;
+    }
+    key[i] = kk;
+  }
   __syncthreads();
   for (int size = 2; size <= np; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -960,13 +937,11 @@ hipError_t launch_prefill(const AttnArgs& a0, int combo, int hd, int bs, int g, 
   const int64_t n_tasks = (int64_t)a.n_seqs * a.n_kv_heads * a.nch * nqb;
   if (n_tasks > (int64_t)1 << 28) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n_tasks);
-  if (a.n_seqs > kInlineOrderMax) {
-    if (bs == 16) {
-      if (hd <= 128) hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 16>), dim3(1), dim3(1024), 0, st, a, order);
-      else hipLaunchKernelGGL((prefill_order_kernel<tile_of(256), 16>), dim3(1), dim3(1024), 0, st, a, order);
-    } else {
-      hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 32>), dim3(1), dim3(1024), 0, st, a, order);
-    }
+  if (bs == 16) {
+    if (hd <= 128) hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 16>), dim3(1), dim3(1024), 0, st, a, order);
+    else hipLaunchKernelGGL((prefill_order_kernel<tile_of(256), 16>), dim3(1), dim3(1024), 0, st, a, order);
+  } else {
+    hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 32>), dim3(1), dim3(1024), 0, st, a, order);
   }
   {
     const hipError_t e0 = hipGetLastError();

@@ -188,9 +188,10 @@ def test_prefill_more_sequences_than_the_order_sort_holds():
     compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_of(w), "4100 seqs decode")
 
 
-def test_prefill_sorted_by_a_separate_kernel():
-    """100 sequences: more than a prefill workgroup ranks by itself (64), so
-    a separate kernel sorts them longest first; results match the oracle."""
+def test_prefill_hundred_sequences():
+    """100 sequences of mixed lengths, sorted longest first by the order
+    kernel before the prefill workgroups pick them up; results match the
+    oracle."""
     w = wgen.make_custom(seed=43, n_seqs=100, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
                          fmts=("f16", "q8_0", "f16"), ctx=(1, 300), mode="kv_map", n_runs=3, kind="prefill",
                          q_per_seq=(1, 8), hole_frac=0.05)
