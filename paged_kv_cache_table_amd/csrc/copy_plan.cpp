@@ -150,42 +150,51 @@ void order_moves(const Move* eff, int64_t m, int32_t* order, uint64_t* work) {
   }
   const uint64_t range = (uint64_t)(hi - lo) + 1;
   const int br = bits_for(range), bi = bits_for((uint64_t)m);
-  int64_t placed = 0;
-  for (int up = 1; up >= 0; --up) {
-    if (2 * br + bi <= 64) {
-      uint64_t* v = work;
-      uint64_t* tmp = work + m;
-      int64_t n = 0;
-      for (int64_t k = 0; k < m; ++k) {
-        const Move& x = eff[k];
-        if ((x.d > x.s) != (up == 1)) continue;
-        uint64_t a = (uint64_t)(x.s - lo), b = (uint64_t)(x.d - lo);
-        if (up) {
-          a = range - 1 - a;
-          b = range - 1 - b;
-        }
-        v[n++] = (a << (br + bi)) | (b << bi) | (uint64_t)k;
-      }
-      v = radix_sort(v, tmp, n, br + bi, 2 * br + bi);
-      for (int64_t i = 0; i < n;) {  // equal src keys: order the run on (dst key, position)
+  if (2 * br + bi <= 64) {
+    // one pass builds both key lists without branching: every move's keys
+    // are written, and only its own list's count advances
+    uint64_t* vu = work;          // upward moves: descending keys, as ascending complements
+    uint64_t* vd = work + m;      // downward moves
+    uint64_t* tmp = work + 2 * m;
+    int64_t nu = 0, nd = 0;
+    for (int64_t k = 0; k < m; ++k) {
+      const Move& x = eff[k];
+      const uint64_t a = (uint64_t)(x.s - lo), b = (uint64_t)(x.d - lo);
+      const int up = x.d > x.s;
+      vu[nu] = ((range - 1 - a) << (br + bi)) | ((range - 1 - b) << bi) | (uint64_t)k;
+      vd[nd] = (a << (br + bi)) | (b << bi) | (uint64_t)k;
+      nu += up;
+      nd += 1 - up;
+    }
+    int64_t placed = 0;
+    const uint64_t pmask = ((uint64_t)1 << bi) - 1;
+    for (int up = 1; up >= 0; --up) {
+      const int64_t n = up ? nu : nd;
+      // radix sort on the src key alone (stable: positions stay in order),
+      // then runs of equal src keys on (dst key, position)
+      uint64_t* v = radix_sort(up ? vu : vd, tmp, n, br + bi, 2 * br + bi);
+      for (int64_t i = 0; i < n;) {
         int64_t j = i + 1;
         while (j < n && (v[j] >> (br + bi)) == (v[i] >> (br + bi))) ++j;
         if (j - i > 1) std::sort(v + i, v + j);
         i = j;
       }
-      const uint64_t pmask = ((uint64_t)1 << bi) - 1;
       for (int64_t i = 0; i < n; ++i) order[placed++] = (int32_t)(v[i] & pmask);
-    } else {
-      int64_t n0 = placed;
-      for (int64_t k = 0; k < m; ++k)
-        if ((eff[k].d > eff[k].s) == (up == 1)) order[placed++] = (int32_t)k;
-      std::stable_sort(order + n0, order + placed, [&](int32_t x, int32_t y) {
-        const Move &a = eff[x], &b = eff[y];
-        if (a.s != b.s) return up ? a.s > b.s : a.s < b.s;
-        if (a.d != b.d) return up ? a.d > b.d : a.d < b.d;
-        return false;
-      });
+      if (up) tmp = vu;  // vu's storage is free once its order is out
     }
+    return;
+  }
+  int64_t placed = 0;
+  for (int up = 1; up >= 0; --up) {
+    const int64_t n0 = placed;
+    for (int64_t k = 0; k < m; ++k)
+      if ((eff[k].d > eff[k].s) == (up == 1)) order[placed++] = (int32_t)k;
+    std::stable_sort(order + n0, order + placed, [&](int32_t x, int32_t y) {
+      const Move &a = eff[x], &b = eff[y];
+      if (a.s != b.s) return up ? a.s > b.s : a.s < b.s;
+      if (a.d != b.d) return up ? a.d > b.d : a.d < b.d;
+      return false;
+    });
   }
 }
 
@@ -312,8 +321,9 @@ void stage_plan(const Move* eff, int64_t m, const Shape& sh, const int32_t* orde
   // rows read from a row that is also written go through the stage; the
   // scatter pairs go to the plan right after room for the most gather pairs
   // (2 per changed row) and the gather pairs, built apart, go in front
+  const int64_t nw = (n_rows + 63) / 64;
   int64_t n_changed = 0;
-  for (int64_t w = 0; w < (n_rows + 63) / 64; ++w) {
+  for (int64_t w = 0; w < nw; ++w) {
     uint64_t bits = 0;
     const int64_t c0 = 64 * w, c1 = std::min<int64_t>(c0 + 64, n_rows);
     for (int64_t c = c0; c < c1; ++c) bits |= (uint64_t)(prov[c] != (int32_t)c) << (c - c0);
@@ -323,22 +333,26 @@ void stage_plan(const Move* eff, int64_t m, const Shape& sh, const int32_t* orde
   std::fill(stage_of, stage_of + n_rows, -1);
   int32_t* scatter = plan + 2 * n_changed;
   int32_t n_stage = 0, n_scatter = 0;
-  for (int64_t c = 0; c < n_rows; ++c) {
-    const int32_t src = prov[c];
-    if (src == (int32_t)c) continue;
-    int32_t y = row_of(src);
-    if ((changed[src >> 6] >> (src & 63)) & 1) {  // the source row is overwritten too
-      int32_t& slot = stage_of[src];
-      if (slot < 0) {
-        gather[2 * n_stage] = y;
-        gather[2 * n_stage + 1] = n_stage;
-        slot = n_stage++;
-      }
-      y = -(slot + 1);
+  // the changed rows in order, through their bits; the first read of a
+  // changed source takes the next stage slot (written unconditionally, kept
+  // only then, so the loop does not branch on it)
+  for (int64_t w = 0; w < nw; ++w) {
+    for (uint64_t bits = changed[w]; bits; bits &= bits - 1) {
+      const int64_t c = 64 * w + __builtin_ctzll(bits);
+      const int32_t src = prov[c];
+      const int32_t ysrc = row_of(src);
+      const bool staged = (changed[src >> 6] >> (src & 63)) & 1;  // the source row is overwritten too
+      const int32_t slot0 = stage_of[src];
+      const bool fresh = staged && slot0 < 0;
+      gather[2 * n_stage] = ysrc;
+      gather[2 * n_stage + 1] = n_stage;
+      const int32_t slot = fresh ? n_stage : slot0;
+      stage_of[src] = slot;
+      n_stage += fresh ? 1 : 0;
+      scatter[2 * n_scatter] = row_of(c);
+      scatter[2 * n_scatter + 1] = staged ? -(slot + 1) : ysrc;
+      ++n_scatter;
     }
-    scatter[2 * n_scatter] = row_of(c);
-    scatter[2 * n_scatter + 1] = y;
-    ++n_scatter;
   }
   std::memmove(plan + 2 * n_stage, scatter, (size_t)n_scatter * 2 * sizeof(int32_t));
   std::memcpy(plan, gather, (size_t)n_stage * 2 * sizeof(int32_t));
