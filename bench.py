@@ -53,6 +53,8 @@ _CSRC = "paged_kv_cache_table_amd/csrc/"
 TRAFFIC = {
     "decode3": ("profiles/decode_split_7b_class.traffic.json",
                 (_CSRC + "pkv_internal.hpp", _CSRC + "decode_impl.hpp", _CSRC + "decode_f16.hip")),
+    "decode2": ("profiles/decode_split_smollm_class.traffic.json",
+                (_CSRC + "pkv_internal.hpp", _CSRC + "decode_impl.hpp", _CSRC + "decode_f16.hip")),
     "store4": ("profiles/store_w4.traffic.json",
                (_CSRC + "pkv_internal.hpp", _CSRC + "store.hip")),
     "prefill4": ("profiles/prefill_window_w4.traffic.json",
@@ -423,12 +425,12 @@ def run_decode(cfg, args):
             "kernel": "decode_split_kernel",
             # events bracket the partials half of the call: the one-workgroup
             # plan kernel (when the call is planned) and the split kernel
-            "timed": "decode partials call (decode_plan_kernel + decode_split_kernel), HIP events",
+            "timed": "decode partials call (decode_split_kernel; a decode_plan_kernel first above 256 sequences), HIP events",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic("decode3") if cfg == 3 and not args.split else None,
+            "traffic": stored_traffic(f"decode{cfg}") if f"decode{cfg}" in TRAFFIC and not args.split else None,
             "algorithmic_bytes": int(alg_split),
         },
     }
