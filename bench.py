@@ -5,8 +5,9 @@
 Default workload: decode on the 7B-class batch (64 sequences in 16 groups of
 4 copy-on-write forks sharing a 2048-token prefix, 32 q / 8 kv heads,
 head_dim 128, block 16, f16 K/V, 4096..32768 tokens each).  A step is one
-pkv_paged_attn_decode call (plan, split and log-sum-exp merge kernels) over
-the batch, with all inputs resident in HBM.  Prints one JSON line:
+pkv_paged_attn_decode call (split and log-sum-exp merge kernels; a plan
+kernel first when the call plans more than 256 sequences) over the batch,
+with all inputs resident in HBM.  Prints one JSON line:
 
 * value: effective KV bandwidth = logical K/V bytes the queries attend to
   (B_log: every visible token x kv head, K and V rows) / step time;
@@ -16,8 +17,9 @@ the batch, with all inputs resident in HBM.  Prints one JSON line:
 * pct_of_device_copy: the same rate against a plain device copy measured in
   the same run;
 * roofline: the split kernel's algorithmic bytes / the average duration of
-  the call's partials half (plan + split kernels) from HIP events on the
-  stream it runs on, against the 8 TB/s HBM peak;
+  the call's partials half (the split kernel, and the plan kernel when there
+  is one) from HIP events on the stream it runs on, against the 8 TB/s HBM
+  peak;
 * cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
   workload on this host, with the host's core counts and CPU model.
 
@@ -280,11 +282,12 @@ def decode_partial_rows(w, split, planned_units_min=4 * 2048):
 
 def run_decode(cfg, args):
     """Decode headline: one fused pkv_paged_attn_decode call (split + merge
-    kernels, and the plan kernel for batches of more than 256 sequences) per
-    step.  Three passes over the same inputs after the warm-up: one call at
-    a time between HIP events on the stream the library launches on
-    (event_ms); the two halves of the call (partials = plan + split kernels,
-    then merge) between events, for the dominant-kernel roofline; and last,
+    kernels, and a plan kernel first when the call plans more than 256
+    sequences) per step.  Three passes over the same inputs after the
+    warm-up: one call at a time between HIP events on the stream the library
+    launches on (event_ms); the two halves of the call (partials = split
+    kernel, after the plan kernel if any, then merge) between events, for
+    the dominant-kernel roofline; and last,
     back to back by wall clock (ms_per_step, value)."""
     import torch
 
@@ -403,7 +406,7 @@ def run_decode(cfg, args):
             "split_tokens": int(split),
             "partial_rows": int(rows),
         },
-        "step": "one pkv_paged_attn_decode call (split + merge kernels; a plan kernel first above 256 sequences)",
+        "step": "one pkv_paged_attn_decode call (split + merge kernels; a plan kernel first when the call plans more than 256 sequences)",
         "timing": ("HIP events per call, caches evicted before each call" if cold
                    else "wall clock over back-to-back calls"),
         "queries_per_s": round(w.n_seqs / (ms * 1e-3), 1),
