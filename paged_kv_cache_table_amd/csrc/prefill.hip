@@ -24,15 +24,15 @@
 // Data movement.  A tile is T/BS whole blocks.  Each wave copies its T/8
 // positions of a tile (which lie in one block: one scalar base address per
 // tile, fixed per-lane offsets) straight from HBM into LDS
-// (global_load_lds: no registers in between), two tiles ahead of the
-// compute, into a ring of three tile slots; it then waits for its own copies
+// (global_load_lds: no registers in between), three tiles ahead of the
+// compute, into a ring of four tile slots; it then waits for its own copies
 // only (vmcnt) and prepares its rows (V rows of positions that are not
 // visible zeroed; q8_0 K rows become their int8 codes as f16, which is exact,
 // and the block scales are kept apart as f32), so one barrier per tile
-// suffices.  f16 rows are
-// stored row-major with their 16-byte chunks XOR-swizzled by the row index,
-// which keeps both the score-operand reads and the transposing V reads free
-// of bank conflicts.
+// suffices.  f16 rows are stored row-major with their 16-byte chunks
+// XOR-permuted by a key of the row (swz_key), which keeps the score-operand
+// reads, the transposing V reads and the q8_0 expansion writes free of bank
+// conflicts.
 //
 // Compute.  Scores are computed transposed, S^T = K Q^T, so each lane holds
 // T/4 scores of one row (positions 16 st + 4 g + i): the row's running max
