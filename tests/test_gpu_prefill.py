@@ -156,7 +156,7 @@ def test_prefill_matches_decode_for_last_queries():
     assert err <= 2e-3
 
 
-def test_prefill_workload4_full_size_sampled():
+def test_prefill_workload4_full_size():
     import torch
 
     w = wgen.make(4)
@@ -166,9 +166,9 @@ def test_prefill_workload4_full_size_sampled():
     torch.cuda.synchronize()
     o, l = out.cpu().numpy(), lse.cpu().numpy()
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
-    seqs = [0, 5, 8, 13]  # two span-style and two multi-run sequences
+    seqs = list(range(w.n_seqs))  # every sequence: the span half and the multi-run half
     ro, rl, rows = d.oracle(seqs)
-    compare(o[rows], l[rows], ro, rl, tol_of(w), "w4 full sampled")
+    compare(o[rows], l[rows], ro, rl, tol_of(w), "w4 full size")
 
 
 def test_prefill_more_sequences_than_the_order_sort_holds():
