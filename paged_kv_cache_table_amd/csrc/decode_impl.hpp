@@ -16,7 +16,9 @@
 // workgroup per possible slot.
 // Lane layout: each token row of one kv head is spread over LPT = HD/16
 // lanes (16 elements per lane), a pass covers TPP = 64/LPT tokens, and a
-// 16- or 32-token block takes BS/TPP passes.  The g query heads that share
+// 16- or 32-token block takes BS/TPP passes.  A pass's K and V rows are
+// staged ahead of compute, through an LDS ring filled by HBM->LDS copies
+// (head_dim 128) or a register ring (head_dim 64 and 256).  The g query heads that share
 // the kv head are all computed from the same K/V registers (GQA reads every
 // K/V byte once).  Each lane keeps its own running output for its tokens;
 // the running max is kept per head for the whole wave, so the end of the
@@ -438,12 +440,32 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
   static_assert(BS % TPP == 0, "block size must be a multiple of tokens per pass");
   constexpr int NU = BS / TPP;  // passes per block; a pass is the pipelined unit
   constexpr int KW = KP::KW, VW = VP::VW;
-  // Register ring of one-pass units: as many as fit the instance's budget
-  // next to q, the running outputs and the temporaries; the loads run
-  // RING-1 units ahead of compute.
+  // K/V staging.  head_dim 128: an LDS ring of one-pass units, private to
+  // the wave: a pass's K rows and V rows are contiguous in the (block, kv
+  // head) tile, so each is copied from HBM into its slot by whole 16-byte
+  // lanes (global_load_lds_dwordx4, 1 KiB per instruction) RING-1 units
+  // ahead of compute, and the compute reads the lane's own elements from the
+  // slot; as many slots as keep the instance's waves within the CU's 160 KiB
+  // of LDS (the 7B-class batch: 735-736 µs per step with either staging).
+  // head_dim 64 and 256: a ring of the same units in registers (the loads
+  // themselves run ahead), sized to the instance's register budget, which
+  // measured faster there: the extra LDS round trip of each unit is exposed
+  // on the SmolLM2-like batch (28.8 against 33.6 µs per call) and costs
+  // 0.8% on the long-context one.
+  constexpr bool kLds = HD == 128;
+  constexpr int KPB = TPP * (int)KP::kHeadBytes;  // K bytes of one pass
+  constexpr int VPB = TPP * (int)VP::kHeadBytes;  // V bytes of one pass
+  constexpr int KPB16 = (KPB + 15) / 16 * 16;
+  constexpr int SLOT = KPB16 + VPB;
+  constexpr int NDK = (KPB + 1023) / 1024, NDV = (VPB + 1023) / 1024;
+  constexpr int NDMA = NDK + NDV;  // copy instructions per unit
+  constexpr int kWavesPerCU = 4 * SplitRegs<HD, G, COMBO>::kWaves;
   constexpr int kBudget = SplitRegs<HD, G, COMBO>::kBudget;
-  constexpr int kRingFit = kBudget / (KW + VW);
+  constexpr int kRingFit = kLds ? (160 * 1024 / kWavesPerCU) / SLOT : kBudget / (KW + VW);
   constexpr int RING = kRingFit < 2 ? 2 : (kRingFit > 8 ? 8 : kRingFit);
+  static_assert(!kLds || (RING - 1) * NDMA < 64, "vmcnt range");
+  static_assert(KPB % 16 == 0 && VPB % 16 == 0, "a pass copies whole 16-byte pieces");
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kLds ? RING : 1][kLds ? SLOT : 16];
   constexpr float kEmpty = -1e30f;  // running max before any visible token
 
   const int lane = threadIdx.x, tok = lane / LPT, sub = lane % LPT;
@@ -526,6 +548,27 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
     uint32_t k[KW];
     uint32_t v[VW];
   };
+  // copy unit (j, u) into ring slot r: K then V, 16 bytes per lane and
+  // instruction (the last instruction of each may leave lanes idle)
+  auto copy_unit = [&](int r, int j, int u) {
+    const int32_t blk = __builtin_amdgcn_readlane(myid, j);
+    const unsigned char* kg = kbase + blk * kbb + u * KPB;
+    const unsigned char* vg = vbase + blk * vbb + u * VPB;
+    const uint32_t lk = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&stage[r][0]));
+    const uint32_t lv = lk + KPB16;
+#pragma unroll
+    for (int i = 0; i < NDK; ++i)
+      if (i * 1024 + lane * 16 < KPB) copy16_to_lds(kg, (uint32_t)(i * 1024 + lane * 16), lk + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NDV; ++i)
+      if (i * 1024 + lane * 16 < VPB) copy16_to_lds(vg, (uint32_t)(i * 1024 + lane * 16), lv + i * 1024);
+  };
+  // the lane's elements of the unit in slot r, once its copies have landed
+  auto read_unit = [&](Unit& U, int r) {
+    kp.load_k(&stage[r][tok * KP::kHeadBytes], sub, U.k);
+    VP::load(&stage[r][KPB16 + tok * VP::kHeadBytes], sub, U.v);
+  };
+  // register ring: the lane's elements of unit (j, u) straight from HBM
   auto load_unit = [&](Unit& U, int j, int u) {
     const int32_t blk = __builtin_amdgcn_readlane(myid, j);
     const int slot = u * TPP + tok;
@@ -573,14 +616,15 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
     }
   };
 
-  // Units (one pass each) run in order over the non-hole blocks; loads run
-  // RING-1 units ahead of compute through a ring of RING register buffers.
-  // The ring is unrolled so every buffer keeps a fixed role.  The body has a
-  // fixed number of steps with one exit at its top: an exit in the middle
-  // would become an exec-masked flow block whose join makes the compiler
-  // drain all outstanding loads.  Steps past the last unit load that unit
-  // again (cache hits) and skip the compute, so the number of loads issued
-  // after any unit is fixed and each wait leaves the later loads in flight.
+  // Units (one pass each) run in order over the non-hole blocks; copies (or
+  // loads) run RING-1 units ahead of compute through the ring of RING LDS
+  // slots (or register buffers).  The ring is unrolled so every slot keeps
+  // a fixed role.  The body has a fixed number of steps with one exit at its
+  // top: an exit in the middle would become an exec-masked flow block whose
+  // join makes the compiler drain all outstanding loads.  Steps past the
+  // last unit copy that unit again (cache hits) and skip the compute, so the
+  // number of copies issued after any unit is fixed and each wait leaves the
+  // later copies in flight.
   struct Cursor {
     uint64_t rest;  // blocks after j still to visit
     int j, u;
@@ -600,20 +644,48 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
     lc.u = 0;
     Cursor cc = lc;
     int issued = 0;
-    auto load_next = [&](Unit& U) {
-      load_unit(U, lc.j, lc.u);
-      if (++issued < n_units) advance(lc);
-    };
     const int n_pad = (n_units + RING - 1) / RING * RING;
-    Unit buf[RING];
+    if constexpr (kLds) {
+      auto copy_next = [&](int r) {
+        copy_unit(r, lc.j, lc.u);
+        if (++issued < n_units) advance(lc);
+      };
 #pragma unroll
-    for (int r = 0; r < RING - 1; ++r) load_next(buf[r]);
-    for (int i = 0; i < n_pad; i += RING) {
+      for (int r = 0; r < RING - 1; ++r) copy_next(r);
+      for (int i = 0; i < n_pad; i += RING) {
 #pragma unroll
-      for (int r = 0; r < RING; ++r) {
-        load_next(buf[(r + RING - 1) % RING]);
-        if (cc.j < 64) compute(buf[r], cc.j, cc.u);
-        advance(cc);
+        for (int r = 0; r < RING; ++r) {
+          // slot (r - 1) mod RING was read by the previous step's compute,
+          // which waited for those reads before using them
+          copy_next((r + RING - 1) % RING);
+          // the RING - 1 units copied after unit r may still be in flight
+          wait_vm<(RING - 1) * NDMA>();
+          asm volatile("" ::: "memory");
+          if (cc.j < 64) {
+            Unit U;
+            read_unit(U, r);
+            compute(U, cc.j, cc.u);
+          }
+          advance(cc);
+        }
+      }
+      // no copy may land in LDS after the wave ends
+      wait_vm<0>();
+    } else {
+      auto load_next = [&](Unit& U) {
+        load_unit(U, lc.j, lc.u);
+        if (++issued < n_units) advance(lc);
+      };
+      Unit buf[RING];
+#pragma unroll
+      for (int r = 0; r < RING - 1; ++r) load_next(buf[r]);
+      for (int i = 0; i < n_pad; i += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) {
+          load_next(buf[(r + RING - 1) % RING]);
+          if (cc.j < 64) compute(buf[r], cc.j, cc.u);
+          advance(cc);
+        }
       }
     }
   }

@@ -291,4 +291,28 @@ struct CowArgs {
 // Grid (n_ops, 2, ceil(largest block bytes / 8 KiB)) x 256 threads.
 hipError_t launch_cow_apply(const CowArgs& a, hipStream_t st);
 
+// HBM -> LDS copies (global_load_lds): each lane's bytes land at lds + lane *
+// size.  Issued as inline assembly so that the compiler, which cannot tell
+// which LDS reads they may alias, adds no waits of its own; kernels wait for
+// them explicitly (wait_vm) before reading the copied bytes.  M0 is named
+// as clobbered (the generated code writes it right before these copies).
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes from base + off (base wave-uniform, off per lane) to lds + 16 * lane.
+// Callers derive base and lds from readfirstlane results only, so both are
+// scalar registers.
+__device__ __forceinline__ void copy16_to_lds(const unsigned char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (GFX9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace pkv

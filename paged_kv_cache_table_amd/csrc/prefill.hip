@@ -146,31 +146,6 @@ __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t 
 
 __device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// HBM -> LDS copies (global_load_lds): each lane's bytes land at lds + lane *
-// size.  Issued as inline assembly so that the compiler, which cannot tell
-// which LDS reads they may alias, adds no waits of its own; the kernel waits
-// for them explicitly (wait_vm) before a barrier publishes the data.  M0 is
-// named as clobbered; nothing else in this file keeps a value in M0 (the
-// generated code only writes it right before these copies).
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// 16 bytes from base + off (base wave-uniform, off per lane) to lds + 16 * lane.
-// Callers derive base and lds from readfirstlane results only, so both are
-// scalar registers.
-__device__ __forceinline__ void copy16_to_lds(const unsigned char* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (GFX9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups): each
 // swap exchanges the odd rows (or the upper half) of one copy of the value
 // with the even rows (lower half) of another copy, so the two registers then
