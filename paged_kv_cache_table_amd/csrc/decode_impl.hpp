@@ -440,29 +440,33 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
   static_assert(BS % TPP == 0, "block size must be a multiple of tokens per pass");
   constexpr int NU = BS / TPP;  // passes per block; a pass is the pipelined unit
   constexpr int KW = KP::KW, VW = VP::VW;
-  // K/V staging.  head_dim 128: an LDS ring of one-pass units, private to
-  // the wave: a pass's K rows and V rows are contiguous in the (block, kv
-  // head) tile, so each is copied from HBM into its slot by whole 16-byte
-  // lanes (global_load_lds_dwordx4, 1 KiB per instruction) RING-1 units
-  // ahead of compute, and the compute reads the lane's own elements from the
-  // slot; as many slots as keep the instance's waves within the CU's 160 KiB
-  // of LDS (the 7B-class batch: 735-736 µs per step with either staging).
-  // head_dim 64 and 256: a ring of the same units in registers (the loads
-  // themselves run ahead), sized to the instance's register budget, which
-  // measured faster there: the extra LDS round trip of each unit is exposed
-  // on the SmolLM2-like batch (28.8 against 33.6 µs per call) and costs
-  // 0.8% on the long-context one.
-  constexpr bool kLds = HD == 128;
+  // K/V staging.  head_dim 128 (16-bit and q8_0 rows): an LDS ring of two
+  // one-pass units, private to the wave: a pass's K rows and V rows are
+  // contiguous in the (block, kv head) tile, so each is copied from HBM into
+  // its slot by whole 16-byte lanes (global_load_lds_dwordx4, 1 KiB per
+  // instruction) one unit ahead of compute, and the compute reads the lane's
+  // own elements from the slot.
+  // On the 7B-class batch two slots measured 737-738 us per step back to
+  // back (748.5 us for one cold call), three slots 741-742 (748-754), and a
+  // ring of the same units in registers 735-736: the three waves per SIMD
+  // keep enough bytes in flight, and a deeper ring only adds to them.
+  // head_dim 64 and 256: the register ring (the loads themselves run
+  // ahead), sized to the instance's register budget, which measured faster
+  // there: the extra LDS round trip of each unit is exposed on the
+  // SmolLM2-like batch (28.8 against 33.6 us per call) and costs 0.8% on the
+  // long-context one.
   constexpr int KPB = TPP * (int)KP::kHeadBytes;  // K bytes of one pass
   constexpr int VPB = TPP * (int)VP::kHeadBytes;  // V bytes of one pass
   constexpr int KPB16 = (KPB + 15) / 16 * 16;
   constexpr int SLOT = KPB16 + VPB;
   constexpr int NDK = (KPB + 1023) / 1024, NDV = (VPB + 1023) / 1024;
   constexpr int NDMA = NDK + NDV;  // copy instructions per unit
-  constexpr int kWavesPerCU = 4 * SplitRegs<HD, G, COMBO>::kWaves;
+  // the LDS ring where two slots per wave fit the CU's 160 KiB at the
+  // instance's occupancy (f32 rows do not)
+  constexpr bool kLds = HD == 128 && 4 * SplitRegs<HD, G, COMBO>::kWaves * 2 * SLOT <= 160 * 1024;
   constexpr int kBudget = SplitRegs<HD, G, COMBO>::kBudget;
-  constexpr int kRingFit = kLds ? (160 * 1024 / kWavesPerCU) / SLOT : kBudget / (KW + VW);
-  constexpr int RING = kRingFit < 2 ? 2 : (kRingFit > 8 ? 8 : kRingFit);
+  constexpr int kRingFit = kBudget / (KW + VW);
+  constexpr int RING = kLds ? 2 : (kRingFit < 2 ? 2 : (kRingFit > 8 ? 8 : kRingFit));
   static_assert(!kLds || (RING - 1) * NDMA < 64, "vmcnt range");
   static_assert(KPB % 16 == 0 && VPB % 16 == 0, "a pass copies whole 16-byte pieces");
   __shared__ __attribute__((aligned(16))) unsigned char stage[kLds ? RING : 1][kLds ? SLOT : 16];
@@ -652,6 +656,13 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
       };
 #pragma unroll
       for (int r = 0; r < RING - 1; ++r) copy_next(r);
+      // The compiler does not count the copies (inline assembly) among the
+      // loads in flight.  Waiting here for everything issued so far (q, then
+      // the first RING - 1 units) is what tells it that q has arrived;
+      // otherwise it would place waits for q at q's first use inside the
+      // loop, where in hardware they would also wait for every copy the ring
+      // has in flight, on every step.
+      wait_vm<0>();
       for (int i = 0; i < n_pad; i += RING) {
 #pragma unroll
         for (int r = 0; r < RING; ++r) {

@@ -473,11 +473,16 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     asm volatile("" ::: "memory");
     const uint32_t mine = (uint32_t)(d.vm >> pw0) & ((1u << PPW) - 1u);
     if (mine != (1u << PPW) - 1u) {
+      // The zero is made here: a zero vector hoisted out of the loop gets
+      // spilled, and the wait for its reload would also wait for every copy
+      // in flight (the load counter is in order).
+      uint32_t z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
       for (int i = 0; i < Gm::NV; ++i) {
         const int uu = i * 64 + l;
         const int r = pw0 + uu / Gm::CHR;
-        if (!((d.vm >> r) & 1ull)) *(uint4*)&sm.v[sl][r * Gm::ROWB + (uu % Gm::CHR) * 16] = make_uint4(0u, 0u, 0u, 0u);
+        if (!((d.vm >> r) & 1ull)) *(uint4*)&sm.v[sl][r * Gm::ROWB + (uu % Gm::CHR) * 16] = make_uint4(z, z, z, z);
       }
     }
     if constexpr (KQ8) {
