@@ -24,8 +24,9 @@ with all inputs resident in HBM.  Prints one JSON line:
   workload on this host, with the host's core counts and CPU model.
 
 Other workloads (for the record; the default is the headline): decode1,
-decode2, decode5, prefill4, copy5b, store4, cow3, defrag3, int4; and calib, a plain device copy of known
-size used to scale the HBM byte counters.
+decode2, decode5, prefill4 (--prefill-k f16: the same batch with f16 K),
+copy5b, store4, cow3, defrag3, int4; and calib, a plain device copy of
+known size used to scale the HBM byte counters.
 
 Counter summary (turns two rocprofv3 --pmc runs, FETCH_SIZE then WRITE_SIZE,
 of a workload and of the calibration copy into bytes per launch):
@@ -497,7 +498,12 @@ def run_prefill(args):
     from workloads import gen as wgen
 
     w = wgen.make(4)
-    log(f"[bench] workload 4: {w.name}; generating inputs on the GPU")
+    kfmt = getattr(args, "prefill_k", "q8_0")
+    if kfmt != w.k_fmt:
+        # the same batch with K stored in another format (what the q8_0 K
+        # format costs the kernel); inputs are regenerated in that format
+        w.k_fmt = kfmt
+    log(f"[bench] workload 4: {w.name}, K {w.k_fmt}; generating inputs on the GPU")
     q, k, v = wgen.materialize(w, "cuda")
     dev = {n: torch.from_numpy(np.ascontiguousarray(x).astype(np.int32)).cuda()
            for n, x in (("table", w.block_table), ("lens", w.seq_lens), ("cu_q", w.cu_q), ("q_pos", w.q_pos),
@@ -540,14 +546,14 @@ def run_prefill(args):
         "metric": "windowed prefill: TFLOP/s (% MFMA f16 peak) and HBM GB/s",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16 (K q8_0)", "data": "synthetic",
+        "dtype": f"f16 (K {w.k_fmt})", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.n_seqs} seqs x {max_q} queries, 32 q / 8 kv heads, hd 128, block 32, "
-                               "K q8_0, V f16; half one span, half 4 runs; causal in window; cache flushed per step",
+                               f"K {w.k_fmt}, V f16; half one span, half 4 runs; causal in window; cache flushed per step",
                    "visible_pairs": pairs, "flops": flops, "kv_bytes": kv_bytes},
         "roofline": {"bound": "mfma", "kernel": "prefill_order_kernel + prefill_kernel + prefill_merge_kernel (one call)",
                      "achieved": round(tflops, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": stored_traffic("prefill4"), "hbm_GBps": round(io_bytes / (ms * 1e-3) / 1e9, 1),
+                     "traffic": stored_traffic("prefill4") if w.k_fmt == "q8_0" else None, "hbm_GBps": round(io_bytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "event_ms": {"median": round(float(np.median(times)), 5), "p10": round(float(np.percentile(times, 10)), 5),
                      "p90": round(float(np.percentile(times, 90)), 5)},
@@ -959,6 +965,8 @@ def main(argv=None):
                     choices=["decode1", "decode2", "decode3", "decode5", "prefill4", "copy5b", "store4", "cow3", "defrag3", "int4", "calib"])
     ap.add_argument("--pmc-summary", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"))
     ap.add_argument("--split", type=int, default=0, help="decode split size in tokens (0 = automatic)")
+    ap.add_argument("--prefill-k", default="q8_0", choices=["q8_0", "f16"],
+                    help="K format of the prefill4 batch (q8_0 as the workload states; f16 for comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args(argv)
