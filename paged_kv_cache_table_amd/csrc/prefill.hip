@@ -710,6 +710,11 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   };
   static_assert(AH <= 3, "wait_tiles covers at most two tiles in flight");
   if (ntl > 0) {
+    // The compiler does not count the copies (inline assembly) among the
+    // loads in flight: this wait tells it that the loads above (q, table
+    // entries) are done, so it places no wait for their registers after the
+    // copies, where in hardware that wait would also cover the copies.
+    wait_vm<0>();
     for (int i = 0; i < AH && i < ntl; ++i) issue(i, i);
     wait_tiles((ntl < AH ? ntl : AH) - 1);
     prepare(0, 0, tile_at(0));
