@@ -173,12 +173,17 @@ hipError_t launch_decode_split(const AttnArgs& a, int combo, int hd, int bs, int
 
 hipError_t launch_decode_merge(const AttnArgs& a, int hd, hipStream_t st) {
   const dim3 grid((unsigned)((a.n_q_heads * hd + 255) / 256), a.n_seqs);
+  const bool small = (int64_t)grid.x * grid.y < 512;  // eight waves share each workgroup's rows
+#define PKV_MERGE(HD)                                                                   \
+  if (small) hipLaunchKernelGGL((decode_merge_kernel<HD, 8>), grid, dim3(512), 0, st, a); \
+  else hipLaunchKernelGGL((decode_merge_kernel<HD, 4>), grid, dim3(256), 0, st, a);
   switch (hd) {
-    case 64: hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL(decode_merge_kernel<256>, grid, dim3(256), 0, st, a); break;
+    case 64: PKV_MERGE(64) break;
+    case 128: PKV_MERGE(128) break;
+    case 256: PKV_MERGE(256) break;
     default: return hipErrorInvalidValue;
   }
+#undef PKV_MERGE
   return hipGetLastError();
 }
 

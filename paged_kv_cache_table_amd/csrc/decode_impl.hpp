@@ -752,16 +752,20 @@ hipError_t launch_split_instance(const AttnArgs& a, int64_t max_units, hipStream
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, lse = (M + log2 L) ln 2.
 // A workgroup takes 256 consecutive (q head, dim) outputs of one sequence,
 // each lane four of them (16-byte loads, so a wave loads 1 KiB of a partial
-// row at once); its four waves share the rows (wave w takes rows w, w + 4,
+// row at once); its NW waves share the rows (wave w takes rows w, w + NW,
 // ..., in order, with a running max, the loads of four rows issued before
-// their arithmetic) and wave 0 combines the four results in wave order
-// through LDS.  Fixed order for a given shape, so results are
+// their arithmetic) and wave 0 combines the NW results in wave order
+// through LDS.  NW = 8 where the grid is small (fewer than 512
+// workgroups: each sequence's rows are walked in fewer dependent rounds),
+// else 4 (SmolLM2-like merge 7.7 against 8.3 us per launch, long context
+// 13.7 against 15.2; the 7B-class batch, 1,024 workgroups, 11.0 against
+// 12.9 with eight).  Fixed order for a given shape, so results are
 // deterministic.  A run's non-empty slots and their pieces hold one
 // contiguous range of rows, found from the run's bounds exactly as the plan
 // places them.
-template <int HD>
-__global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
-  constexpr int kUnroll = 4, kWaves = 4;
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_merge_kernel(AttnArgs a) {
+  constexpr int kUnroll = 4, kWaves = NW;
   __shared__ float part[kWaves - 1][6][64];
   const int s = blockIdx.y;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
