@@ -451,10 +451,9 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
   // ring of the same units in registers 735-736: the three waves per SIMD
   // keep enough bytes in flight, and a deeper ring only adds to them.
   // head_dim 64 and 256: the register ring (the loads themselves run
-  // ahead), sized to the instance's register budget, which measured faster
-  // there: the extra LDS round trip of each unit is exposed on the
-  // SmolLM2-like batch (28.8 against 33.6 us per call) and costs 0.8% on the
-  // long-context one.
+  // ahead), sized to the instance's register budget; the LDS ring measured
+  // the same there (SmolLM2-like 34.0-34.2 against 34.1-34.2 us per call,
+  // long context 1466-1467 against 1465-1466 us per step).
   constexpr int KPB = TPP * (int)KP::kHeadBytes;  // K bytes of one pass
   constexpr int VPB = TPP * (int)VP::kHeadBytes;  // V bytes of one pass
   constexpr int KPB16 = (KPB + 15) / 16 * 16;
