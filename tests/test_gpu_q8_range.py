@@ -144,3 +144,22 @@ def test_q8_store_then_prefill_large_values(e):
         out, lse = d.prefill() if kind == "prefill" else d.decode()
         ro, rl = d.oracle()
         compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, 2e-3, f"store 2^{e} then {kind}")
+
+
+@pytest.mark.parametrize("band", ["sub", 15])
+def test_q8_scale_band_f32_queries(band):
+    """The f32-query combination (q f32, K q8_0, V f32) at the ends of the
+    scale range: decode, and prefill (which runs f32 queries through the
+    decode kernels), against the oracle."""
+    e = _band_exp(band)
+    rng = np.random.default_rng(700 + BANDS.index(band))
+    for kind, mode in (("decode", "causal"), ("prefill", "kv_map")):
+        w = wgen.make_custom(seed=710 + BANDS.index(band), n_seqs=4, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                             block_size=16, fmts=("f32", "q8_0", "f32"), ctx=(30, 300), mode=mode, n_runs=4,
+                             kind=kind, q_per_seq=(1, 30), hole_frac=0.05)
+        w.scale = float(2.4e-3 * 2.0 ** -e)
+        log(f"q8_0 scale band 2^{e} ({band}), f32 q and V: {kind} {mode}, attention scale {w.scale:.3g}")
+        d = _dev_with_pool(w, rng, [band])
+        out, lse = d.prefill() if kind == "prefill" else d.decode()
+        ro, rl = d.oracle()
+        compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, 2e-3, f"f32 band {band} {kind} {mode}")
