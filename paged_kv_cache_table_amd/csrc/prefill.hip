@@ -67,9 +67,6 @@ constexpr float kLazyMax = 8.0f;    // log2 growth of a row max that forces a re
 constexpr int kTargetTasks = 384;   // workgroups the chunking aims for (1.5 per CU)
 constexpr int kMaxChunks = 16;      // unless a chunk would exceed kMaxTiles
 constexpr int kMaxTiles = 256;      // tiles of one workgroup's chunk (its list lives in LDS)
-constexpr int kFuseMax = 4;         // chunks the last chunk merges itself; more use the merge launch
-constexpr int kSc1 = 16;            // buffer access cache policy: sc1, coherent across the device
-constexpr int kBufFlags = 0x00020000;  // buffer resource word 3: raw 32-bit dwords
 
 // One tile of a workgroup's chunk, described once before the main loop: its
 // first position (a multiple of the tile size), the visibility mask of its
@@ -118,7 +115,6 @@ struct __attribute__((aligned(16))) PrefillSmem {
   unsigned char raw[KQ8 ? kRing : 1][KQ8 ? kPWaves * Gm::RAWW : 16];  // q8_0 tiles as stored
   TileRec tiles[kMaxTiles];                                           // this workgroup's chunk
   int32_t lim_max[kPWaves];                                           // each wave's largest causal limit
-  int32_t last;                                                       // this chunk arrived last (fused merge)
 };
 
 // Row r's 16-byte chunks are stored XOR-permuted by a key of the row so that
@@ -215,8 +211,7 @@ template <int HD, int BS, int G, bool KQ8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t* __restrict__ window,
                     const unsigned char* __restrict__ kpool, const unsigned char* __restrict__ vpool,
-                    const int32_t* __restrict__ order, uint32_t* __restrict__ arrivals, int32_t n_tasks,
-                    int32_t nqb) {
+                    const int32_t* __restrict__ order, int32_t n_tasks, int32_t nqb) {
   using Gm = PGeom<HD>;
   constexpr int T = Gm::T;
   constexpr int RT = Gm::RT;
@@ -739,23 +734,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   }
   if (bad && (a.flags & PKV_FLAG_CHECKED) && a.err && kvh == 0 && qb == 0 && t == 0) atomicAdd(a.err, bad);
 
-  // ---- finish: sum the row's lane groups; write the output or the partial.
-  // With arrival counters (at most kFuseMax chunks) the chunk's partials are
-  // written through to the device's coherence point (sc1 buffer stores, so no
-  // cache of one XCD holds them), the workgroup counts itself in, and the
-  // chunk that arrives last merges the chunks' partials of its rows itself,
-  // in chunk order, with the same arithmetic as prefill_merge_kernel.
-  const bool fuse = arrivals != nullptr;
-  const int64_t row_lo = (int64_t)j0 * a.n_q_heads + kvh * G;  // this workgroup's first row
-  const uint32_t span = (uint32_t)((int64_t)(j1 - 1 - j0) * a.n_q_heads + G);  // rows from row_lo on
-  // buffer resources over the span's partials (used only with arrival
-  // counters, where the host has checked span * nch * HD * 4 < 2^31)
-  const __amdgpu_buffer_rsrc_t rml =
-      __builtin_amdgcn_make_buffer_rsrc(a.part_ml + row_lo * a.nch * 2, 0, (int32_t)(span * a.nch * 8u), kBufFlags);
-  const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(a.part_o + row_lo * a.nch * HD, 0, (int32_t)(span * a.nch * HD * 4u), kBufFlags);
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  // ---- finish: sum the row's lane groups; write the output or the partial
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float ls = o[rt][DT][0];
@@ -771,18 +750,6 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
         *(float4*)(orow + dt * 16 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
       }
       if (a.lse && g == 0) a.lse[row] = empty ? -INFINITY : (m[rt] + __builtin_amdgcn_logf(ls)) * kLn2;
-    } else if (fuse) {
-      const uint32_t pr = (uint32_t)(row - row_lo) * a.nch + c;  // partial row within the workgroup's span
-      if (g == 0) {
-        const float2 ml = make_float2(m[rt], empty ? 0.f : ls);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ml), rml, pr * 8, 0, kSc1);
-      }
-      if (!empty) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[rt][dt]), ro,
-                                                 pr * (HD * 4) + (dt * 16 + 4 * g) * 4, 0, kSc1);
-      }
     } else {
       const int64_t pr = row * a.nch + c;
       if (g == 0) *(float2*)(a.part_ml + pr * 2) = make_float2(m[rt], empty ? 0.f : ls);
@@ -794,98 +761,6 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       }
     }
   }
-  if (!fuse) return;
-  // Every store of this wave has completed at the coherence point; after the
-  // barrier, so have those of the whole workgroup, and only then is the
-  // arrival counted (a relaxed device-scope add: its order after the stores
-  // comes from the waits).
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (t == 0) {
-    const int64_t ci = ((int64_t)rank * a.n_kv_heads + kvh) * nqb + qb;
-    const uint32_t before = __hip_atomic_fetch_add(arrivals + ci, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = before == (uint32_t)(a.nch - 1);
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  // The last chunk: the other chunks' partials are read from the coherence
-  // point (sc1 loads), issued after the count showed every chunk's stores done.
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const float ls = o[rt][DT][0];
-    if (!rok[rt]) continue;
-    const int64_t row = (int64_t)jq[rt] * a.n_q_heads + kvh * G + hq[rt];
-    const uint32_t pr0 = (uint32_t)(row - row_lo) * a.nch;  // chunk 0's partial row
-    // (max, sum) of every chunk, loaded together (index clamped to a chunk
-    // that exists) and chosen by selects; this chunk's own come from registers
-    static_assert(kFuseMax == 4, "the loads below are pinned four at a time");
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    f32x2_t mlv[kFuseMax];
-#pragma unroll
-    for (int cc = 0; cc < kFuseMax; ++cc)
-      mlv[cc] = __builtin_bit_cast(f32x2_t,
-                                   __builtin_amdgcn_raw_buffer_load_b64(rml, (pr0 + (cc < a.nch ? cc : 0)) * 8, 0, kSc1));
-    // used together here, so the four loads are issued back to back (not
-    // each in its own branch behind a wait)
-    asm volatile("" : "+v"(mlv[0]), "+v"(mlv[1]), "+v"(mlv[2]), "+v"(mlv[3]));
-    float mc[kFuseMax], lc[kFuseMax];
-#pragma unroll
-    for (int cc = 0; cc < kFuseMax; ++cc) {
-      mc[cc] = cc >= a.nch ? kEmptyMax : (cc == c ? m[rt] : mlv[cc][0]);
-      lc[cc] = cc >= a.nch ? 0.f : (cc == c ? (m[rt] == kEmptyMax ? 0.f : ls) : mlv[cc][1]);
-    }
-    float M = kEmptyMax;
-#pragma unroll
-    for (int cc = 0; cc < kFuseMax; ++cc)
-      if (cc < a.nch) M = fmaxf(M, mc[cc]);
-    float* orow = a.out + row * HD;
-    if (M == kEmptyMax) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *(float4*)(orow + dt * 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (a.lse && g == 0) a.lse[row] = -INFINITY;
-      continue;
-    }
-    // the other chunks' outputs, loaded CG chunks at a time (all of them in
-    // flight where the registers allow) and summed in chunk order
-    constexpr int CG = DT <= 8 ? kFuseMax : 1;
-    float Ls = 0.f;
-    float4 acc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int c0 = 0; c0 < kFuseMax; c0 += CG) {
-      // loaded only for the other chunks that exist (a uniform test); read
-      // below only for those of them that are not empty
-      float4_t part[CG][DT];
-#pragma unroll
-      for (int cc = c0; cc < c0 + CG; ++cc)
-        if (cc < a.nch && cc != c) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            part[cc - c0][dt] = __builtin_bit_cast(
-                float4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, (pr0 + cc) * (HD * 4) + (dt * 16 + 4 * g) * 4, 0, kSc1));
-        }
-#pragma unroll
-      for (int cc = c0; cc < c0 + CG; ++cc) {
-        if (cc >= a.nch || mc[cc] == kEmptyMax) continue;
-        const float wgt = fast_exp2(mc[cc] - M);
-        Ls += lc[cc] * wgt;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const float4_t v = cc == c ? o[rt][dt] : part[cc - c0][dt];
-          acc[dt].x += wgt * v[0];
-          acc[dt].y += wgt * v[1];
-          acc[dt].z += wgt * v[2];
-          acc[dt].w += wgt * v[3];
-        }
-      }
-    }
-    const float inv = 1.f / Ls;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *(float4*)(orow + dt * 16 + 4 * g) = make_float4(acc[dt].x * inv, acc[dt].y * inv, acc[dt].z * inv, acc[dt].w * inv);
-    if (a.lse && g == 0) a.lse[row] = (M + __builtin_amdgcn_logf(Ls)) * kLn2;
-  }
 }
 
 // Orders the sequences by decreasing number of window tiles (about the
@@ -893,14 +768,10 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
 // sort in LDS.  More than kOrderMax sequences keep their own order.
 constexpr int kOrderMax = 4096;
 
-// It also clears the prefill kernel's arrival counters (n_arrivals of them;
-// the prefill launch that follows on the stream counts into them).
 template <int T, int BS>
-__global__ __launch_bounds__(1024) void prefill_order_kernel(AttnArgs a, int32_t* order, uint32_t* arrivals,
-                                                             int64_t n_arrivals) {
+__global__ __launch_bounds__(1024) void prefill_order_kernel(AttnArgs a, int32_t* order) {
   __shared__ uint64_t key[kOrderMax];
   const int n = a.n_seqs, t = threadIdx.x;
-  for (int64_t i = t; i < n_arrivals; i += 1024) arrivals[i] = 0u;
   if (n > kOrderMax) {
     for (int i = t; i < n; i += 1024) order[i] = i;
     return;
@@ -1014,15 +885,6 @@ int plan_chunks(const AttnArgs& a, int hd, int g) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// query blocks per sequence and arrival counters of a call
-int32_t query_blocks(const AttnArgs& a, int hd, int g) {
-  const int qpb = rows_per_wg(hd) / g;
-  return (a.max_q + qpb - 1) / qpb;
-}
-size_t n_arrivals(const AttnArgs& a, int hd, int g) {
-  return (size_t)a.n_seqs * a.n_kv_heads * query_blocks(a, hd, g);
-}
-
 }  // namespace
 
 size_t prefill_workspace(const AttnArgs& a, int combo, int hd, int bs, int g, bool* found) {
@@ -1030,12 +892,10 @@ size_t prefill_workspace(const AttnArgs& a, int combo, int hd, int bs, int g, bo
   *found = combo == kComboF16 || combo == kComboQ8H;
   if (!*found) return 0;
   const int nch = plan_chunks(a, hd, g);
-  // sequence order, then (when nch > 1) one arrival counter per (sequence,
-  // kv head, query block), (max, sum) and output partials
+  // sequence order, then (max, sum) and output partials when nch > 1
   size_t need = align256((size_t)a.n_seqs * sizeof(int32_t));
   if (nch > 1) {
     const size_t rows = (size_t)a.n_q_total * a.n_q_heads * nch;
-    need += align256(n_arrivals(a, hd, g) * sizeof(uint32_t));
     need += align256(rows * 2 * sizeof(float)) + align256(rows * hd * sizeof(float));
   }
   if (a.flags & PKV_FLAG_CHECKED) need += 256;
@@ -1052,34 +912,21 @@ hipError_t launch_prefill(const AttnArgs& a0, int combo, int hd, int bs, int g, 
   unsigned char* base = (unsigned char*)a0.part_o;
   int32_t* order = (int32_t*)base;
   base += align256((size_t)a.n_seqs * sizeof(int32_t));
-  const int qpb = rows_per_wg(hd) / g;
-  const int32_t nqb = query_blocks(a, hd, g);
-  // The last chunk of each query block merges the partials itself when there
-  // are few chunks and a workgroup's partial rows fit 32-bit buffer offsets;
-  // otherwise a merge launch follows.
-  uint32_t* arrivals = nullptr;
-  int64_t n_arr = 0;
   if (a.nch > 1) {
     const size_t rows = (size_t)a.n_q_total * a.n_q_heads * a.nch;
-    const int64_t span = ((int64_t)(qpb - 1) * a.n_q_heads + g) * a.nch * hd * 4;
-    if (a.nch <= kFuseMax && span < ((int64_t)1 << 31)) {
-      arrivals = (uint32_t*)base;
-      n_arr = (int64_t)n_arrivals(a, hd, g);
-    }
-    base += align256(n_arrivals(a, hd, g) * sizeof(uint32_t));
     a.part_ml = (float*)base;
     a.part_o = (float*)(base + align256(rows * 2 * sizeof(float)));
   }
+  const int qpb = rows_per_wg(hd) / g;
+  const int32_t nqb = (a.max_q + qpb - 1) / qpb;
   const int64_t n_tasks = (int64_t)a.n_seqs * a.n_kv_heads * a.nch * nqb;
   if (n_tasks > (int64_t)1 << 28) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n_tasks);
   if (bs == 16) {
-    if (hd <= 128)
-      hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 16>), dim3(1), dim3(1024), 0, st, a, order, arrivals, n_arr);
-    else
-      hipLaunchKernelGGL((prefill_order_kernel<tile_of(256), 16>), dim3(1), dim3(1024), 0, st, a, order, arrivals, n_arr);
+    if (hd <= 128) hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 16>), dim3(1), dim3(1024), 0, st, a, order);
+    else hipLaunchKernelGGL((prefill_order_kernel<tile_of(256), 16>), dim3(1), dim3(1024), 0, st, a, order);
   } else {
-    hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 32>), dim3(1), dim3(1024), 0, st, a, order, arrivals, n_arr);
+    hipLaunchKernelGGL((prefill_order_kernel<tile_of(128), 32>), dim3(1), dim3(1024), 0, st, a, order);
   }
   {
     const hipError_t e0 = hipGetLastError();
@@ -1089,10 +936,10 @@ hipError_t launch_prefill(const AttnArgs& a0, int combo, int hd, int bs, int g, 
   if (hd == HD && bs == BS && g == G) {                                                           \
     if (q8)                                                                                       \
       hipLaunchKernelGGL((prefill_kernel<HD, BS, G, true>), grid, dim3(512), 0, st, a, a.table,   \
-                         a.window, a.k_pool, a.v_pool, order, arrivals, (int32_t)n_tasks, nqb);   \
+                         a.window, a.k_pool, a.v_pool, order, (int32_t)n_tasks, nqb);             \
     else                                                                                          \
       hipLaunchKernelGGL((prefill_kernel<HD, BS, G, false>), grid, dim3(512), 0, st, a, a.table,  \
-                         a.window, a.k_pool, a.v_pool, order, arrivals, (int32_t)n_tasks, nqb);   \
+                         a.window, a.k_pool, a.v_pool, order, (int32_t)n_tasks, nqb);             \
     *found = true;                                                                                \
   }
 #define PKV_PCASES_G(HD, BS) PKV_PCASE(HD, BS, 1) PKV_PCASE(HD, BS, 2) PKV_PCASE(HD, BS, 3) PKV_PCASE(HD, BS, 4) PKV_PCASE(HD, BS, 8)
@@ -1104,7 +951,7 @@ hipError_t launch_prefill(const AttnArgs& a0, int combo, int hd, int bs, int g, 
 #undef PKV_PCASE
   if (!*found) return hipSuccess;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nch == 1 || arrivals) return e;
+  if (e != hipSuccess || a.nch == 1) return e;
   const int rpb = 256 / (hd / 4);
   const dim3 mgrid((unsigned)(((int64_t)a.max_q * a.n_q_heads + rpb - 1) / rpb), (unsigned)a.n_seqs);
   if (hd == 64) hipLaunchKernelGGL(prefill_merge_kernel<64>, mgrid, dim3(256), 0, st, a);
