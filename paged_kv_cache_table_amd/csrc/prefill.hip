@@ -471,12 +471,6 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
   auto prepare = [&](int sl, int kb, const TileD& d) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    // The lane's offsets below are recomputed for every tile from a lane
-    // index the compiler cannot see through: kept live across the loop they
-    // get spilled, and the wait for a reload would also wait for every copy
-    // in flight.
-    int ll = l;
-    asm volatile("" : "+v"(ll));
     const uint32_t mine = (uint32_t)(d.vm >> pw0) & ((1u << PPW) - 1u);
     if (mine != (1u << PPW) - 1u) {
       // The zero is made here: a zero vector hoisted out of the loop gets
@@ -486,7 +480,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
       asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
       for (int i = 0; i < Gm::NV; ++i) {
-        const int uu = i * 64 + ll;
+        const int uu = i * 64 + l;
         const int r = pw0 + uu / Gm::CHR;
         if (!((d.vm >> r) & 1ull)) *(uint4*)&sm.v[sl][r * Gm::ROWB + (uu % Gm::CHR) * 16] = make_uint4(z, z, z, z);
       }
@@ -494,7 +488,7 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     if constexpr (KQ8) {
 #pragma unroll
       for (int e = 0; e < Gm::NQ8; ++e) {
-        const int uq = e * 64 + ll;
+        const int uq = e * 64 + l;
         if (uq < PPW * Gm::UPR) {
           const int p = uq / Gm::UPR, rem = uq - p * Gm::UPR;
           const int bq = rem >> 1, h = rem & 1;
@@ -583,83 +577,130 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     }
   };
 
-  // Online softmax of one 32-position half (half kh of tile d; the order of
-  // the halves does not matter): hidden positions score -inf, the running max
-  // moves lazily (only when a row's max would grow by more than 2^8, so p
-  // stays <= 256, exact enough in f16, and the output is rarely rescaled),
-  // and the probabilities are rounded to f16 as the B operand of the PV step.
-  auto softmax = [&](float (&sc)[RT][8], const TileD& d, int kh, half8_t (&pf)[RT]) {
-    const uint32_t vmh = (uint32_t)(d.vm >> (32 * kh));
-    const int32_t t0h = d.t0 + 32 * kh;
-    const bool full = vmh == 0xffffffffu && t0h + 32 <= lim_min_w;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (!full) {
-        // score jj is position p = 16 (jj / 4) + 4 g + jj % 4 of the half
-        const uint32_t vg = vmh >> (4 * g);
-        const int32_t lr = lim[rt] - t0h - 4 * g;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int pc = 16 * (jj >> 2) + (jj & 3);
-          const bool ok = ((vg >> pc) & 1u) && pc < lr;
-          sc[rt][jj] = ok ? sc[rt][jj] : -INFINITY;
-        }
-      }
-      float mx = sc[rt][0];
-#pragma unroll
-      for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[rt][jj]);
-      // A row grows iff one of its lanes holds a score above the threshold
-      // (scaling by mul > 0 keeps the order), so the row max across the
-      // lane groups is only formed when some row of the wave grows.
-      if (__builtin_amdgcn_ballot_w64(mx * mul > m[rt] + kLazyMax)) {
-        const float mc = max_over_groups(mx) * mul;
-        const bool grow = mc > m[rt] + kLazyMax;
-        const float mn = grow ? mc : m[rt];
-        const float alpha = fast_exp2(m[rt] - mn);
-#pragma unroll
-        for (int dt = 0; dt <= DT; ++dt) o[rt][dt] *= alpha;
-        m[rt] = mn;
-      }
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) pf[rt][jj] = (_Float16)fast_exp2(fmaf(sc[rt][jj], mul, -m[rt]));
-  };
-
-  // O^T += V^T P^T for half kh of V tile vt: two transposing reads give lane
-  // (g, n16) column dt*16 + n16 of V at positions 16 h + 4 g + e of the half
-  // (operand element 4 h + e); lane n16 addresses row 16 h + 4 g + n16 / 4 of
-  // the half at columns dt*16 + 4 (n16 % 4) ...  The row sums of the rounded
-  // probabilities come from one more MFMA whose A operand is all ones.
-  auto pv = [&](const unsigned char* vt, int kh, const half8_t (&pf)[RT]) {
+  // One tile, in 32-position halves: the online softmax is exact in any
+  // order, so each half updates the running max/sum and the output in turn.
+  // The scores of the next half (matrix cores) are issued after the running
+  // max of the current half and interleaved with its exponentials (vector
+  // ALU), so the two overlap.
+  auto compute = [&](int sl, int kb, const TileD& d) {
+    const unsigned char* kt = KQ8 ? sm.k[kb] : sm.k[sl];
+    const float* ksl = &sm.ksc[KQ8 ? kb : 0][0][0];
+    const unsigned char* vt = sm.v[sl];
     const half8_t ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
                           (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+    float sc[RT][8], sn[RT][8];
+    scores(kt, ksl, 0, sn);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      half8_t vf;
+    for (int kh = 0; kh < NKH; ++kh) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int R = 32 * kh + 16 * h + 4 * g + (n16 >> 2);
-        const int cb = 32 * dt + 8 * (n16 & 3);  // byte offset of the 4 columns in the row
-        const int off = swz<HD>(R, cb >> 4) + (cb & 15);
-        const short4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)&vt[off]);
-        const half2_t* hx = (const half2_t*)&x;
-        vf[4 * h + 0] = hx[0][0];
-        vf[4 * h + 1] = hx[0][1];
-        vf[4 * h + 2] = hx[1][0];
-        vf[4 * h + 3] = hx[1][1];
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sc[rt][jj] = sn[rt][jj];
+      const uint32_t vmh = (uint32_t)(d.vm >> (32 * kh));
+      const int32_t t0h = d.t0 + 32 * kh;
+      const bool full = vmh == 0xffffffffu && t0h + 32 <= lim_min_w;
+
+      // ---- online softmax per row (the four lane groups hold the same row).
+      // The running max moves lazily: only when a row's max would grow by
+      // more than 2^8, so p stays <= 256 (exact enough in f16) and the output
+      // is rarely rescaled.  Hidden positions score -inf and so get p = 0.
+      half8_t pf[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (!full) {
+          // score jj is position p = 16 (jj / 4) + 4 g + jj % 4 of the half
+          const uint32_t vg = vmh >> (4 * g);
+          const int32_t lr = lim[rt] - t0h - 4 * g;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int pc = 16 * (jj >> 2) + (jj & 3);
+            const bool ok = ((vg >> pc) & 1u) && pc < lr;
+            sc[rt][jj] = ok ? sc[rt][jj] : -INFINITY;
+          }
+        }
+        float mx = sc[rt][0];
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[rt][jj]);
+        // A row grows iff one of its lanes holds a score above the threshold
+        // (scaling by mul > 0 keeps the order), so the row max across the
+        // lane groups is only formed when some row of the wave grows.
+        if (__builtin_amdgcn_ballot_w64(mx * mul > m[rt] + kLazyMax)) {
+          const float mc = max_over_groups(mx) * mul;
+          const bool grow = mc > m[rt] + kLazyMax;
+          const float mn = grow ? mc : m[rt];
+          const float alpha = fast_exp2(m[rt] - mn);
+#pragma unroll
+          for (int dt = 0; dt <= DT; ++dt) o[rt][dt] *= alpha;
+          m[rt] = mn;
+        }
       }
+      // the next half's scores (matrix cores) next to this half's
+      // exponentials (vector ALU): one basic block, so they interleave
+      if (kh + 1 < NKH) scores(kt, ksl, kh + 1, sn);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma16x16x32(vf, pf[rt], o[rt][dt]);
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pf[rt][jj] = (_Float16)fast_exp2(fmaf(sc[rt][jj], mul, -m[rt]));
+
+      // ---- O^T += V^T P^T: two transposing reads give lane (g, n16) column
+      // dt*16 + n16 of V at positions 16 h + 4 g + e of the half (operand
+      // element 4 h + e); lane n16 addresses row 16 h + 4 g + n16 / 4 of the
+      // half at columns dt*16 + 4 (n16 % 4) ...  The wave raises its priority
+      // for these matrix instructions, so the two waves of a SIMD drift apart
+      // and one's vector work overlaps the other's matrix work.
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        half8_t vf;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int R = 32 * kh + 16 * h + 4 * g + (n16 >> 2);
+          const int cb = 32 * dt + 8 * (n16 & 3);  // byte offset of the 4 columns in the row
+          const int off = swz<HD>(R, cb >> 4) + (cb & 15);
+          const short4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)&vt[off]);
+          const half2_t* hx = (const half2_t*)&x;
+          vf[4 * h + 0] = hx[0][0];
+          vf[4 * h + 1] = hx[0][1];
+          vf[4 * h + 2] = hx[1][0];
+          vf[4 * h + 3] = hx[1][1];
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma16x16x32(vf, pf[rt], o[rt][dt]);
+      }
+      // row sums of the rounded probabilities (every element of o[rt][DT])
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) o[rt][DT] = mfma16x16x32(ones, pf[rt], o[rt][DT]);
+      __builtin_amdgcn_s_setprio(0);
+      // Issue order of this block (a scheduling hint; no effect on values):
+      // the K fragment reads run four ahead of the matrix instructions that
+      // use them, three vector instructions (the exponentials) sit between
+      // each pair of score MFMAs, and the V reads of the PV step again run
+      // four ahead.  Masks: 0x100 LDS read, 0x008 MFMA, 0x002 vector ALU.
+      if (kh + 1 < NKH) {
+        constexpr int kSM = 2 * KS * RT;             // score MFMAs of a half
+        constexpr int kSR = 2 * KS * (KQ8 ? 2 : 1);  // their K fragment (and q8_0 scale) reads
+        constexpr int kPM = (DT + 1) * RT;                // PV and row-sum MFMAs
+        constexpr int kPR = 2 * DT;                       // V reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < kSM / 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          if (i < kSR - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < kPM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < kPR - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
     }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) o[rt][DT] = mfma16x16x32(ones, pf[rt], o[rt][DT]);
   };
 
-  // ---- pipeline.  Tile t lives in V (and copied K) slot t % kRing and, for
-  // q8_0, in expanded-K slot t & 1; the copies of a tile are issued kRing - 1
-  // tiles ahead of its first use.
+  // ---- pipeline: tile k is computed while tile k+1 is being prepared and
+  // tiles k+2 .. k+kRing-1 are being copied; tile t lives in slot t % kRing;
+  // one barrier per tile
   constexpr int AH = kRing - 1;  // tiles whose copies run ahead of the computed one
   // wait until at most n tiles' copies of this wave are still in flight
   auto wait_tiles = [&](int n) {
@@ -678,109 +719,17 @@ void prefill_kernel(AttnArgs a, const int32_t* __restrict__ table, const int32_t
     wait_tiles((ntl < AH ? ntl : AH) - 1);
     prepare(0, 0, tile_at(0));
     __syncthreads();
-    if constexpr (NKH == 1) {
-      // one half per tile: scores, softmax and PV of tile k while tile k+1 is
-      // prepared and tiles k+2 .. k+kRing-1 are copied; one barrier per tile
-      float sc[RT][8];
-      half8_t pf[RT];
-      for (int k = 0;; ++k) {
-        if (k + AH < ntl) issue((k + AH) % kRing, k + AH);
-        const TileD d = tile_at(k);
-        scores(KQ8 ? sm.k[k & 1] : sm.k[k % kRing], &sm.ksc[KQ8 ? (k & 1) : 0][0][0], 0, sc);
-        softmax(sc, d, 0, pf);
-        __builtin_amdgcn_s_setprio(1);
-        pv(sm.v[k % kRing], 0, pf);
-        __builtin_amdgcn_s_setprio(0);
-        // prepare tile k+1 once this wave's copies of it have landed
-        if (k + 1 < ntl) {
-          const int later = ntl - (k + 2);  // tiles issued after k+1 that may still be in flight
-          wait_tiles(later < AH - 1 ? later : AH - 1);
-          prepare((k + 1) % kRing, (k + 1) & 1, tile_at(k + 1));
-        }
-        __syncthreads();
-        if (k + 1 >= ntl) break;
+    for (int k = 0;; ++k) {
+      if (k + AH < ntl) issue((k + AH) % kRing, k + AH);
+      compute(k % kRing, k & 1, tile_at(k));
+      // prepare tile k+1 once this wave's copies of it have landed
+      if (k + 1 < ntl) {
+        const int later = ntl - (k + 2);  // tiles issued after k+1 that may still be in flight
+        wait_tiles(later < AH - 1 ? later : AH - 1);
+        prepare((k + 1) % kRing, (k + 1) & 1, tile_at(k + 1));
       }
-    } else {
-      // Two halves per tile, and the two waves of a SIMD take turns (waves w
-      // and w + 4 share a SIMD): half h is a matrix phase M(h) (the PV step
-      // of half h - 1, then the scores of half h) followed by a vector phase
-      // V(h) (its softmax).  Waves 0-3 run M(h) in barrier interval 2h and
-      // V(h) in 2h + 1, waves 4-7 one interval later, so in every interval
-      // one wave of a SIMD feeds the matrix cores while the other does vector
-      // work.  Per tile t (halves 2t, 2t + 1): each wave prepares its
-      // positions of tile t + 1 in V(2t) (intervals 4t + 1 and 4t + 2), after
-      // the last read of the expanded-K slot it rewrites (the scores of half
-      // 2t - 1, interval 4t - 1) and before the first read of tile t + 1
-      // (interval 4t + 4); the copies of tile t + 3 are issued in V(2t + 1)
-      // (intervals 4t + 3 and 4t + 4), after the last read of their slot's
-      // previous tile (the PV step of half 2t - 1 by waves 4-7, interval
-      // 4t + 1).  Every wave passes the same number of barriers, 2 H + 2.
-      static_assert(NKH == 2, "two halves per tile");
-      const bool late = w >= kPWaves / 2;
-      const int H = ntl * NKH;
-      float sc[RT][8];
-      half8_t pf[RT];
-      auto kslot = [&](int tt) { return KQ8 ? sm.k[tt & 1] : sm.k[tt % kRing]; };
-      auto sslot = [&](int tt) { return &sm.ksc[KQ8 ? (tt & 1) : 0][0][0]; };
-      auto vphase = [&](int h) {
-        const int tt = h >> 1, kh = h & 1;
-        softmax(sc, tile_at(tt), kh, pf);
-        if (kh == 0) {
-          if (tt + 1 < ntl) {
-            // tile tt + 2, issued before tile tt + 1's first use, may still be in flight
-            wait_tiles(tt + 2 < ntl ? 1 : 0);
-            prepare((tt + 1) % kRing, (tt + 1) & 1, tile_at(tt + 1));
-          }
-        } else if (tt + AH < ntl) {
-          issue((tt + AH) % kRing, tt + AH);
-        }
-        __syncthreads();
-      };
-      if (late) __syncthreads();
-      __builtin_amdgcn_s_setprio(1);
-      scores(kslot(0), sslot(0), 0, sc);
-      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
-      vphase(0);
-      for (int h = 1; h < H; ++h) {
-        // one basic block: the PV step of half h - 1 and the scores of half h
-        const int tt = h >> 1, kh = h & 1;
-        __builtin_amdgcn_s_setprio(1);
-        pv(sm.v[((h - 1) >> 1) % kRing], (h - 1) & 1, pf);
-        scores(kslot(tt), sslot(tt), kh, sc);
-        __builtin_amdgcn_s_setprio(0);
-        // Issue order (a scheduling hint; no effect on values): the LDS reads
-        // run four ahead of the matrix instructions that use them, and each
-        // pair of q8_0 score MFMAs is followed by the scale FMAs of the pair
-        // before it.  Masks: 0x100 LDS read, 0x008 MFMA, 0x002 vector ALU.
-        {
-          constexpr int kPR = 2 * DT;                      // V reads
-          constexpr int kPM = (DT + 1) * RT;               // PV and row-sum MFMAs
-          constexpr int kSR = 2 * KS * (KQ8 ? 2 : 1);      // K fragment (and q8_0 scale) reads
-          constexpr int kSM = 2 * KS * RT;                 // score MFMAs
-          constexpr int kRd = kPR + kSR;
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-          for (int i = 0; i < kPM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (4 + i < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < kSM / 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (KQ8 && i > 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            if (4 + kPM + i < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          if (KQ8) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        }
-        __syncthreads();
-        vphase(h);
-      }
-      __builtin_amdgcn_s_setprio(1);
-      pv(sm.v[((H - 1) >> 1) % kRing], (H - 1) & 1, pf);
-      __builtin_amdgcn_s_setprio(0);
-      __syncthreads();
-      if (!late) __syncthreads();
+      if (k + 1 >= ntl) break;
     }
   }
   if (bad && (a.flags & PKV_FLAG_CHECKED) && a.err && kvh == 0 && qb == 0 && t == 0) atomicAdd(a.err, bad);
