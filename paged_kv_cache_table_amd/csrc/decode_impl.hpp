@@ -481,6 +481,8 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
   int s, kvh;
   int32_t lo, hi;
   int64_t prow;
+  int32_t spec = -1;       // this lane's table entry, read ahead (direct causal calls)
+  bool have_spec = false;
   if (a.self_plan) {
     const uint32_t unit = blockIdx.x;
     const uint32_t item = unit / (uint32_t)a.n_kv_heads;
@@ -511,6 +513,14 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
     kvh = blockIdx.x;
     const int slot = blockIdx.y;
     s = blockIdx.z;
+    if (a.mode == PKV_WIN_CAUSAL) {
+      // Causal: slot k covers [k split, (k + 1) split) cut at the sequence
+      // length, so its table entries do not wait for the length; they are
+      // read beside it (entries past the cut are neither used nor checked).
+      const int32_t b = slot * (a.split / BS) + lane;
+      if (lane < a.split / BS && b < a.max_blocks) spec = a.table[(int64_t)s * a.max_blocks + b];
+      have_spec = true;
+    }
     split_range(a, s, slot, clamp_seq_len(a.seq_lens[s], a.max_blocks, BS), lo, hi);
     if (lo >= hi) return;  // not a work item
     prow = (int64_t)s * a.rows_per_seq + slot;
@@ -519,7 +529,19 @@ __global__ __launch_bounds__(64, (SplitRegs<HD, G, COMBO>::kWaves)) void decode_
   const int32_t jb0 = lo / BS;
   const int32_t nblk = (hi - 1) / BS - jb0 + 1;  // <= 64 by construction
   int32_t myid = -1;
-  if (lane < nblk) myid = block_id(a, s, jb0 + lane, kvh == 0);
+  if (have_spec) {
+    // the entry read ahead, checked as block_id checks it (slot k starts at
+    // block jb0 = k split / BS, so lane i holds block jb0 + i)
+    if (lane < nblk) {
+      myid = spec;
+      if (myid < 0 || myid >= a.n_pool_blocks) {
+        if (kvh == 0 && myid != PKV_INVALID_BLOCK_ID && (a.flags & PKV_FLAG_CHECKED) && a.err) atomicAdd(a.err, 1);
+        myid = -1;
+      }
+    }
+  } else if (lane < nblk) {
+    myid = block_id(a, s, jb0 + lane, kvh == 0);
+  }
   // q is read while the block ids are in flight
   KP kp;
   const int64_t qoff = ((int64_t)s * a.n_q_heads + (int64_t)kvh * G) * HD;
